@@ -1,0 +1,228 @@
+// C ABI of libsfv: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/sfv.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SFV_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SFV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int check_attn_dims(int B1, int N, int L, int Hq, int Hkv, int d) {
+  if (B1 < 1 || B1 > SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "B1=%d not in [1, %d]", B1, SFV_MAX_BRANCHES);
+  if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
+  if (L < 0) return fail(SFV_E_INVAL, "L=%d < 0", L);
+  if (Hq < 1 || Hkv < 1) return fail(SFV_E_INVAL, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(SFV_E_INVAL, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!pow2_group(Hq / Hkv)) return fail(SFV_E_UNSUPPORTED, "group size Hq/Hkv=%d not in {1,2,4,8}", Hq / Hkv);
+  if (d != 32 && d != 64 && d != 128) return fail(SFV_E_UNSUPPORTED, "head dim d=%d not in {32,64,128}", d);
+  const double rows = (double)B1 * N * Hq;
+  if (rows * d > 2e9 || (double)Hkv * L * d > 2e9) return fail(SFV_E_INVAL, "tensor too large");
+  return SFV_OK;
+}
+
+// Validates the tree and fills the by-value description the kernels use.
+int make_tree(const int32_t* parent_host, int B1, sfv::TreeArgs* tree) {
+  if (!parent_host) return fail(SFV_E_INVAL, "parent_host is NULL");
+  if (B1 < 1 || B1 > SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "B1=%d not in [1, %d]", B1, SFV_MAX_BRANCHES);
+  if (parent_host[0] != -1) return fail(SFV_E_TREE, "parent[0]=%d, must be -1", parent_host[0]);
+  std::memset(tree, 0, sizeof(*tree));
+  tree->B1 = B1;
+  tree->depth[0] = 0;
+  tree->parent[0] = -1;
+  int maxd = 0;
+  for (int i = 1; i < B1; ++i) {
+    const int p = parent_host[i];
+    if (p < 0 || p >= i) return fail(SFV_E_TREE, "parent[%d]=%d not in [0, %d)", i, p, i);
+    tree->parent[i] = (signed char)p;
+    tree->depth[i] = (signed char)(tree->depth[p] + 1);
+    if (tree->depth[i] > maxd) maxd = tree->depth[i];
+  }
+  tree->levels = maxd + 1;
+  int pos = 0;
+  for (int lv = 0; lv <= maxd; ++lv) {
+    tree->level_start[lv] = (unsigned char)pos;
+    for (int i = 0; i < B1; ++i)
+      if (tree->depth[i] == lv) tree->by_level[pos++] = (unsigned char)i;
+  }
+  tree->level_start[maxd + 1] = (unsigned char)pos;
+  return SFV_OK;
+}
+
+int commit_items_max(const sfv::TreeArgs& tree, int N, int M, bool noisy) {
+  if (!noisy) return M;
+  long bound = 0;
+  for (int lv = 0; lv < tree.levels; ++lv) {
+    const int width = tree.level_start[lv + 1] - tree.level_start[lv];
+    bound += (long)N * ((width + sfv::kItemRowsHost - 1) / sfv::kItemRowsHost);
+  }
+  return bound < M ? (int)bound : M;
+}
+
+int check_commit_dims(int B1, int N, int M, int V) {
+  if (B1 < 1 || B1 > SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "B1=%d not in [1, %d]", B1, SFV_MAX_BRANCHES);
+  if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
+  if (M < 0 || M > B1 * N) return fail(SFV_E_INVAL, "M=%d not in [0, B1*N=%d]", M, B1 * N);
+  if (V < 1) return fail(SFV_E_INVAL, "V=%d < 1", V);
+  if (V % 8 != 0) return fail(SFV_E_UNSUPPORTED, "V=%d is not a multiple of 8", V);
+  if (V >= (1 << 28)) return fail(SFV_E_UNSUPPORTED, "V=%d too large", V);
+  return SFV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sfv_last_error(void) { return g_err; }
+
+int sfv_version(void) { return 100; }
+
+int sfv_attend_workspace_bytes(int B1, int N, int L, int Hq, int Hkv, int d, size_t* bytes) {
+  if (!bytes) return fail(SFV_E_INVAL, "bytes is NULL");
+  const int rc = check_attn_dims(B1, N, L, Hq, Hkv, d);
+  if (rc != SFV_OK) return rc;
+  *bytes = sfv::attn_plan(B1, N, L, Hq, Hkv, d).ws_bytes;
+  return ok();
+}
+
+int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk, const void* k_ctx,
+                        const void* v_ctx, int B1, int N, int L, int Hq, int Hkv, int d,
+                        float softmax_scale, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int rc = check_attn_dims(B1, N, L, Hq, Hkv, d);
+  if (rc != SFV_OK) return rc;
+  if (!q || !k_blk || !v_blk || !o || !lse) return fail(SFV_E_INVAL, "null tensor pointer");
+  if (L > 0 && (!k_ctx || !v_ctx)) return fail(SFV_E_INVAL, "null context pointer with L=%d", L);
+  if (!std::isfinite(softmax_scale)) return fail(SFV_E_INVAL, "softmax_scale is not finite");
+  const sfv::AttnPlan plan = sfv::attn_plan(B1, N, L, Hq, Hkv, d);
+  if (workspace_bytes < plan.ws_bytes) {
+    return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
+  }
+  if (plan.ws_bytes > 0 && !workspace) return fail(SFV_E_INVAL, "workspace is NULL");
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_blk | (uintptr_t)v_blk | (uintptr_t)k_ctx |
+                       (uintptr_t)v_ctx | (uintptr_t)o | (uintptr_t)workspace;
+  if (al % 16 != 0) return fail(SFV_E_INVAL, "tensor pointers must be 16-byte aligned");
+  return hip_status(sfv::launch_attention(q, k_blk, v_blk, k_ctx, v_ctx, B1, N, L, Hq, Hkv, d,
+                                          softmax_scale, o, lse, workspace, plan,
+                                          (hipStream_t)stream),
+                    "sfv_attend_branches");
+}
+
+int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t* count, void* stream) {
+  if (!state || !rows || !count) return fail(SFV_E_INVAL, "null pointer");
+  if (B1 < 1 || B1 > SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "B1=%d not in [1, %d]", B1, SFV_MAX_BRANCHES);
+  if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
+  return hip_status(sfv::launch_masked_rows(state, B1, N, rows, count, (hipStream_t)stream),
+                    "sfv_masked_rows");
+}
+
+int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R, const void* w, int D, int V,
+                float* logits, void* stream) {
+  if (M < 0) return fail(SFV_E_INVAL, "M=%d < 0", M);
+  if (R < 1) return fail(SFV_E_INVAL, "R=%d < 1", R);
+  if (D < 1 || V < 1) return fail(SFV_E_INVAL, "D=%d, V=%d must be positive", D, V);
+  if (D % 64 != 0) return fail(SFV_E_UNSUPPORTED, "D=%d is not a multiple of 64", D);
+  if ((double)M * V >= 9.0e15 || (double)V * D >= 9.0e15) return fail(SFV_E_INVAL, "too large");
+  if (M > 0 && (!hidden || !rows || !w || !logits)) return fail(SFV_E_INVAL, "null tensor pointer");
+  const uintptr_t al = (uintptr_t)hidden | (uintptr_t)w | (uintptr_t)logits;
+  if (al % 16 != 0) return fail(SFV_E_INVAL, "tensor pointers must be 16-byte aligned");
+  return hip_status(sfv::launch_lm_head(hidden, rows, M, R, w, D, V, logits, (hipStream_t)stream),
+                    "sfv_lm_head");
+}
+
+int sfv_commit_workspace_bytes(int B1, int N, int M, int V, size_t* bytes) {
+  if (!bytes) return fail(SFV_E_INVAL, "bytes is NULL");
+  const int rc = check_commit_dims(B1, N, M, V);
+  if (rc != SFV_OK) return rc;
+  // Worst case over trees and temperatures: M items (T = 0 uses exactly M).
+  const sfv::CommitPlan a = sfv::commit_plan(B1, N, M, V, M, false);
+  size_t worst = a.ws_bytes;
+  for (int items = 1; items <= M; items = items < 16 ? items + 1 : items * 2) {
+    const sfv::CommitPlan b = sfv::commit_plan(B1, N, M, V, items, true);
+    if (b.ws_bytes > worst) worst = b.ws_bytes;
+  }
+  const sfv::CommitPlan c = sfv::commit_plan(B1, N, M, V, M, true);
+  if (c.ws_bytes > worst) worst = c.ws_bytes;
+  *bytes = worst;
+  return ok();
+}
+
+int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
+               const int32_t* parent_host, int B1, int N, int V, float temperature, uint64_t seed,
+               uint64_t step0, int64_t pos0, int k_max, float tau, int32_t* next_state,
+               int32_t* commit_pos, int32_t* token, float* conf, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  (void)tau;
+  int rc = check_commit_dims(B1, N, M, V);
+  if (rc != SFV_OK) return rc;
+  if (!state || !next_state || !commit_pos || !workspace) return fail(SFV_E_INVAL, "null pointer");
+  if (M > 0 && (!logits || !rows || !token || !conf)) return fail(SFV_E_INVAL, "null pointer");
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) {
+    return fail(SFV_E_INVAL, "temperature must be finite and >= 0");
+  }
+  if (k_max < 1) return fail(SFV_E_INVAL, "k_max=%d < 1", k_max);
+  if (k_max != 1) return fail(SFV_E_UNSUPPORTED, "k_max=%d: only one position per step", k_max);
+  if ((uintptr_t)logits % 16 != 0) return fail(SFV_E_INVAL, "logits must be 16-byte aligned");
+  sfv::TreeArgs tree;
+  rc = make_tree(parent_host, B1, &tree);
+  if (rc != SFV_OK) return rc;
+  const bool noisy = temperature > 0.f;
+  const int items = commit_items_max(tree, N, M, noisy);
+  const sfv::CommitPlan plan = sfv::commit_plan(B1, N, M, V, items, noisy);
+  if (workspace_bytes < plan.ws_bytes) {
+    return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
+  }
+  return hip_status(sfv::launch_commit(logits, rows, M, state, tree, N, V, temperature, seed, step0,
+                                       pos0, next_state, commit_pos, token, conf, workspace, plan,
+                                       (hipStream_t)stream),
+                    "sfv_commit");
+}
+
+int sfv_match_tree(const int32_t* state, const int32_t* next_state, const int32_t* commit_pos,
+                   const int32_t* parent_host, int B1, int N, int k_max, int S_max, int32_t* chain,
+                   int32_t* n_accepted, int32_t* status, void* stream) {
+  if (!state || !next_state || !commit_pos || !chain || !n_accepted || !status) {
+    return fail(SFV_E_INVAL, "null pointer");
+  }
+  if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
+  if (k_max < 1) return fail(SFV_E_INVAL, "k_max=%d < 1", k_max);
+  sfv::TreeArgs tree;
+  const int rc = make_tree(parent_host, B1, &tree);
+  if (rc != SFV_OK) return rc;
+  return hip_status(sfv::launch_match(state, next_state, commit_pos, tree, N, k_max, S_max, chain,
+                                      n_accepted, status, (hipStream_t)stream),
+                    "sfv_match_tree");
+}
+
+int sfv_selfcheck_bounds(double* out, void* stream) {
+  if (!out) return fail(SFV_E_INVAL, "out is NULL");
+  return hip_status(sfv::launch_selfcheck(out, (hipStream_t)stream), "sfv_selfcheck_bounds");
+}
+
+}  // extern "C"

@@ -1,0 +1,707 @@
+// Commit of every branch: token per masked row (greedy or Gumbel-max with
+// counter-based noise shared by branches of equal depth), max-softmax
+// confidence, and the per-branch unmask-argmax.  Also the masked-row scan.
+//
+// SPOT ("On the SPOT: ... Commit-Order Prediction"): exact decoding commits
+// one masked position per target pass ("Important context", commit order);
+// the drafter and the target share per-position Gumbel noise, so given the
+// noise the target's transition is deterministic (coupled-noise match,
+// Proposition 2).  SpecFold, introduction: an unmasking rule picks the
+// high-confidence masked positions.
+//
+// Exactness: tokens and committed positions must equal the CPU definition
+// bit for bit.  The vocabulary sweep runs a fast fp32 path with a proven
+// error bound and re-decides exactly whatever falls inside the bound:
+//  * Gumbel keys: each lane evaluates g with hardware log2 (error below
+//    kGumbelEps, certified over all 2^32 words by sfv_selfcheck_bounds); the
+//    running best key of the wave is shared every 8 ids and any id whose fast
+//    key comes within the margin of it is re-evaluated with fp64 logarithms,
+//    exactly as defined.  The exact argmax is always among those.
+//  * S = sum exp(l - max l): fp32 exp2 terms summed in fp64, with a running
+//    bound E on |S - S_exact|.  A branch whose best and runner-up intervals
+//    [S - E, S + E] overlap is re-decided from S summed with fp64 exp.
+// This translation unit is compiled with -ffp-contract=off.
+#include "common.h"
+#include "internal.h"
+
+namespace sfv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerIter = 8 * kThreads;  // vocab ids per workgroup iteration
+constexpr int kItemRows = 8;            // rows sharing one noise sweep
+constexpr float kLog2e = 1.44269504088896341f;
+
+// Error model of one fast term t = exp2(fl32(fl32(x - m) * log2e)), relative
+// to exp(x - m), for a = m - x >= 0:  |t / exp(x - m) - 1| <= kC1 * a + kC2.
+// kC1 covers the two fp32 roundings of the argument, kC2 the hardware exp2
+// (certified below 2^-22 by the self-check; 2^-20 is used).
+constexpr float kC1 = 3.5f / 16777216.0f;
+constexpr float kC2 = 1.0f / 1048576.0f;
+// Bound on |g_fast - g_exact| (certified below 1e-5 by the self-check).
+constexpr float kGumbelEps = 1.0f / 4096.0f;
+
+struct Item {
+  int nrows;
+  int pos;    // block position n
+  int level;  // depth of the rows' branches
+  int rows[kItemRows];
+  int pad;
+};
+
+struct Partial {
+  float lmax;  // max logit in the range
+  int lidx;    // lowest id attaining it
+  float kmax;  // max exact Gumbel key (T > 0)
+  int kidx;    // lowest id attaining it
+  double S;    // sum exp(l - lmax) over the range
+  float E;     // bound on |S - S_exact|
+  int pad;
+};
+
+struct WsLayout {
+  int32_t* rowmap;  // [B1*N] flat position -> row, -1 if not masked
+  int32_t* count;   // [1] work items
+  Item* items;      // [items_max]
+  Partial* part;    // [M][splits]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline WsLayout ws_layout(void* base, int B1, int N, int M, int items_max) {
+  char* b = (char*)base;
+  WsLayout w;
+  size_t off = 0;
+  w.rowmap = (int32_t*)(b + off);
+  off = align256(off + sizeof(int32_t) * (size_t)B1 * N);
+  w.count = (int32_t*)(b + off);
+  off = align256(off + 16);
+  w.items = (Item*)(b + off);
+  off = align256(off + sizeof(Item) * (size_t)items_max);
+  w.part = (Partial*)(b + off);
+  return w;
+}
+
+size_t ws_bytes(int B1, int N, int M, int items_max, int splits) {
+  size_t off = align256(sizeof(int32_t) * (size_t)B1 * N);
+  off = align256(off + 16);
+  off = align256(off + sizeof(Item) * (size_t)items_max);
+  return off + sizeof(Partial) * (size_t)M * splits;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11) and the Gumbel transform.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// The 8 noise words of ids 8*blk .. 8*blk+7: word j = half (j & 1) of output (j >> 1).
+__device__ __forceinline__ void noise_block(uint64_t seed, uint64_t step, uint64_t pos, uint64_t blk,
+                                            unsigned w[8]) {
+  uint64_t c[4] = {blk, pos, step, 0};
+  philox4x64_10(c, seed, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[2 * j] = (unsigned)(c[j] & 0xFFFFFFFFull);
+    w[2 * j + 1] = (unsigned)(c[j] >> 32);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// g = -ln(-ln u), u = (w + 1/2) 2^-32, in fp32 with hardware log2.
+__device__ __forceinline__ float gumbel_fast(unsigned w) {
+  const float ln2 = 0.693147180559945309f;
+  float L1;  // -ln u > 0
+  if (w < 0x80000000u) {
+    const float u = ((float)w + 0.5f) * 2.3283064365386963e-10f;
+    L1 = -fast_log2(u) * ln2;
+  } else {
+    const float e = ((float)(~w) + 0.5f) * 2.3283064365386963e-10f;  // 1 - u, in (0, 1/2]
+    if (e < 0.0078125f) {
+      L1 = e * (1.f + e * (0.5f + e * (0.33333333f + e * 0.25f)));
+    } else {
+      L1 = -fast_log2(1.f - e) * ln2;
+    }
+  }
+  return -fast_log2(L1) * ln2;
+}
+
+// The defined value: fl32(-ln(-ln u)) with both logarithms in fp64.
+__device__ __forceinline__ float gumbel_exact(unsigned w) {
+  const double u = ((double)w + 0.5) * 2.3283064365386962890625e-10;
+  return (float)(-log(-log(u)));
+}
+
+__device__ __forceinline__ double gumbel_exact_f64(unsigned w) {
+  const double u = ((double)w + 0.5) * 2.3283064365386962890625e-10;
+  return -log(-log(u));
+}
+
+// Lexicographic "better" for (value, index): larger value, then lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// ---------------------------------------------------------------------------
+// masked-row scan (one workgroup)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void masked_rows_kernel(const int32_t* state, int total,
+                                                           int32_t* rows, int32_t* count) {
+  __shared__ int wsum[16];
+  __shared__ int base_s;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  if (t == 0) base_s = 0;
+  __syncthreads();
+  for (int f0 = 0; f0 < total; f0 += 1024) {
+    const int f = f0 + t;
+    const int flag = (f < total && state[f] == -1) ? 1 : 0;
+    const unsigned long long bal = __ballot(flag);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base_s;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (flag) rows[off + before] = f;
+    __syncthreads();
+    if (t == 0) {
+      int s = 0;
+      for (int w = 0; w < 16; ++w) s += wsum[w];
+      base_s += s;
+    }
+    __syncthreads();
+  }
+  if (t == 0) *count = base_s;
+}
+
+// ---------------------------------------------------------------------------
+// plan: row map and (for T > 0) work items grouping rows of equal (depth, n)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* rows, int M, int N,
+                                                               TreeArgs tree, bool noisy, WsLayout ws) {
+  __shared__ int tsum[kThreads];
+  const int t = threadIdx.x;
+  const int total = tree.B1 * N;
+  for (int f = t; f < total; f += kThreads) ws.rowmap[f] = -1;
+  __syncthreads();
+  for (int r = t; r < M; r += kThreads) {
+    const int f = rows[r];
+    if (f >= 0 && f < total) ws.rowmap[f] = r;  // ids outside the block are ignored
+  }
+  __syncthreads();
+  if (!noisy) {
+    if (t == 0) *ws.count = M;
+    return;
+  }
+  // pairs p = level * N + n, contiguous ranges per thread
+  const int pairs = tree.levels * N;
+  const int per = (pairs + kThreads - 1) / kThreads;
+  const int pb = t * per, pe = min(pairs, pb + per);
+  int mine = 0;
+  for (int p = pb; p < pe; ++p) {
+    const int lv = p / N, n = p % N;
+    int cnt = 0;
+    for (int a = tree.level_start[lv]; a < tree.level_start[lv + 1]; ++a)
+      cnt += ws.rowmap[tree.by_level[a] * N + n] >= 0;
+    mine += (cnt + kItemRows - 1) / kItemRows;
+  }
+  tsum[t] = mine;
+  __syncthreads();
+  int off = 0;
+  for (int u = 0; u < t; ++u) off += tsum[u];
+  for (int p = pb; p < pe; ++p) {
+    const int lv = p / N, n = p % N;
+    Item it;
+    it.nrows = 0;
+    it.pos = n;
+    it.level = lv;
+    it.pad = 0;
+    for (int a = tree.level_start[lv]; a < tree.level_start[lv + 1]; ++a) {
+      const int r = ws.rowmap[tree.by_level[a] * N + n];
+      if (r < 0) continue;
+      it.rows[it.nrows++] = r;
+      if (it.nrows == kItemRows) {
+        ws.items[off++] = it;
+        it.nrows = 0;
+      }
+    }
+    if (it.nrows > 0) {
+      for (int k = it.nrows; k < kItemRows; ++k) it.rows[k] = -1;
+      ws.items[off++] = it;
+    }
+  }
+  if (t == kThreads - 1) *ws.count = off;
+}
+
+// ---------------------------------------------------------------------------
+// vocabulary sweep of one work item over one vocab range
+// ---------------------------------------------------------------------------
+struct RowsArgs {
+  const float* logits;
+  const int32_t* rows;
+  int M, N, V;
+  int splits, chunk;
+  float inv_t;
+  uint64_t seed, step0, pos0;
+};
+
+template <bool NOISY, int R>
+__global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLayout ws) {
+  __shared__ float red_f[kThreads / kWave][R][2];
+  __shared__ int red_i[kThreads / kWave][R][2];
+  __shared__ double red_d[kThreads / kWave][R];
+  __shared__ float red_e[kThreads / kWave][R];
+  __shared__ float wg_lmax[R];
+
+  const int item = blockIdx.x / a.splits;
+  const int split = blockIdx.x % a.splits;
+  if (item >= *ws.count) return;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+
+  int nrows, row[R];
+  uint64_t step = 0, pos = 0;
+  if (NOISY) {
+    const Item it = ws.items[item];
+    nrows = it.nrows;
+#pragma unroll
+    for (int k = 0; k < R; ++k) row[k] = k < nrows ? it.rows[k] : -1;
+    step = a.step0 + (uint64_t)it.level;
+    pos = a.pos0 + (uint64_t)it.pos;
+  } else {
+    nrows = 1;
+    row[0] = item;
+  }
+
+  const int vb = split * a.chunk;
+  const int ve = min(a.V, vb + a.chunk);
+
+  float lmax[R], E[R], wbest[R], kmax[R];
+  int lidx[R], kidx[R];
+  double S[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    lmax[k] = -INFINITY;
+    lidx[k] = 0x7FFFFFFF;
+    S[k] = 0.0;
+    E[k] = 0.f;
+    wbest[k] = -INFINITY;
+    kmax[k] = -INFINITY;
+    kidx[k] = 0x7FFFFFFF;
+  }
+
+  // The trip count is uniform across the workgroup (cross-lane reductions run
+  // inside the loop); a lane past the range end keeps every value at -inf.
+  for (int v0 = vb; v0 < ve; v0 += kPerIter) {
+    const int v = v0 + 8 * t;
+    const bool active = v < ve;  // ve and v are multiples of 8
+    unsigned wd[8];
+    float gf[8];
+    if (NOISY) {
+      noise_block(a.seed, step, pos, (uint64_t)(v >> 3), wd);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gf[e] = gumbel_fast(wd[e]);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (k >= nrows) break;
+      float4 x0 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY), x1 = x0;
+      if (active) {
+        const float* src = a.logits + (size_t)row[k] * a.V + v;
+        x0 = *(const float4*)src;
+        x1 = *(const float4*)(src + 4);
+      }
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      // running max / first argmax and the confidence sum (this lane's ids)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!active) break;
+        const float xe = x[e];
+        if (xe > lmax[k]) {
+          if (lmax[k] != -INFINITY) {
+            const float af = xe - lmax[k];
+            const float f = fast_exp2(-af * kLog2e);
+            S[k] *= (double)f;
+            E[k] = E[k] * f + (float)S[k] * (kC1 * af + kC2);
+          }
+          lmax[k] = xe;
+          lidx[k] = v + e;
+        }
+        const float am = lmax[k] - xe;
+        const float tt = fast_exp2(-am * kLog2e);
+        S[k] += (double)tt;
+        E[k] += tt * (kC1 * am + kC2);
+      }
+      if (NOISY) {
+        float ka[8], lm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ka[e] = (x[e] * a.inv_t) + gf[e];
+          lm = fmaxf(lm, ka[e]);
+        }
+        wbest[k] = fmaxf(wbest[k], wave_max(lm));
+        const float thr = wbest[k] - (2.f * kGumbelEps + 4.f * 1.1920929e-7f * fabsf(wbest[k]) + 1e-30f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (active && ka[e] >= thr) {
+            const float key = (x[e] * a.inv_t) + gumbel_exact(wd[e]);
+            if (key > kmax[k]) {
+              kmax[k] = key;
+              kidx[k] = v + e;
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- reduce over the workgroup, row by row ----
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (k >= nrows) break;
+    float bm = lmax[k];
+    int bi = lidx[k];
+    float km = kmax[k];
+    int ki = kidx[k];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(bm, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (better(om, oi, bm, bi)) {
+        bm = om;
+        bi = oi;
+      }
+      if (NOISY) {
+        const float okm = __shfl_xor(km, o, kWave);
+        const int oki = __shfl_xor(ki, o, kWave);
+        if (better(okm, oki, km, ki)) {
+          km = okm;
+          ki = oki;
+        }
+      }
+    }
+    if (lane == 0) {
+      red_f[wave][k][0] = bm;
+      red_i[wave][k][0] = bi;
+      red_f[wave][k][1] = km;
+      red_i[wave][k][1] = ki;
+    }
+  }
+  __syncthreads();
+  if (t < R && t < nrows) {
+    float bm = red_f[0][t][0];
+    int bi = red_i[0][t][0];
+    for (int w = 1; w < kThreads / kWave; ++w)
+      if (better(red_f[w][t][0], red_i[w][t][0], bm, bi)) {
+        bm = red_f[w][t][0];
+        bi = red_i[w][t][0];
+      }
+    wg_lmax[t] = bm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (k >= nrows) break;
+    const float M = wg_lmax[k];
+    double s = 0.0;
+    float e = 0.f;
+    if (lmax[k] != -INFINITY) {
+      const double f = exp((double)lmax[k] - (double)M);  // fp64: exact to ~1 ulp
+      s = S[k] * f;
+      e = (float)((double)E[k] * f) + (float)s * 1e-12f;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      s += __shfl_xor(s, o, kWave);
+      e += __shfl_xor(e, o, kWave);
+    }
+    if (lane == 0) {
+      red_d[wave][k] = s;
+      red_e[wave][k] = e;
+    }
+  }
+  __syncthreads();
+  if (t < R && t < nrows) {
+    double s = 0.0;
+    float e = 0.f;
+    float km = red_f[0][t][1];
+    int ki = red_i[0][t][1];
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      s += red_d[w][t];
+      e += red_e[w][t];
+      if (w && better(red_f[w][t][1], red_i[w][t][1], km, ki)) {
+        km = red_f[w][t][1];
+        ki = red_i[w][t][1];
+      }
+    }
+    float bm = red_f[0][t][0];
+    int bi = red_i[0][t][0];
+    for (int w = 1; w < kThreads / kWave; ++w)
+      if (better(red_f[w][t][0], red_i[w][t][0], bm, bi)) {
+        bm = red_f[w][t][0];
+        bi = red_i[w][t][0];
+      }
+    Partial pr;
+    pr.lmax = bm;
+    pr.lidx = bi;
+    pr.kmax = km;
+    pr.kidx = ki;
+    pr.S = s;
+    pr.E = e * 1.0001f + (float)(s * 1e-13);
+    pr.pad = 0;
+    ws.part[(size_t)row[t] * a.splits + split] = pr;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finalize: merge ranges, token/conf per row, unmask-argmax per branch
+// ---------------------------------------------------------------------------
+struct FinArgs {
+  const float* logits;
+  const int32_t* state;
+  int32_t* next_state;
+  int32_t* commit_pos;
+  int32_t* token;
+  float* conf;
+  int N, V, splits;
+  bool noisy;
+};
+
+__global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, WsLayout ws) {
+  __shared__ double sS[kMaxBlock];
+  __shared__ float sE[kMaxBlock];
+  __shared__ float sM[kMaxBlock];
+  __shared__ int sTok[kMaxBlock];
+  __shared__ int sCand[kMaxBlock];
+  __shared__ double red[kThreads / kWave];
+  __shared__ int best_n_s, ncand_s;
+  __shared__ double lo_s, hi_s;
+
+  const int i = blockIdx.x;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int N = a.N;
+  for (int n = t; n < N; n += kThreads) {
+    const int f = i * N + n;
+    sS[n] = -1.0;  // not masked
+    if (a.state[f] != -1) continue;
+    const int r = ws.rowmap[f];
+    if (r < 0) continue;
+    const Partial* pp = ws.part + (size_t)r * a.splits;
+    float M = -INFINITY, km = -INFINITY;
+    int mi = 0x7FFFFFFF, ki = 0x7FFFFFFF;
+    for (int s = 0; s < a.splits; ++s) {
+      if (better(pp[s].lmax, pp[s].lidx, M, mi)) {
+        M = pp[s].lmax;
+        mi = pp[s].lidx;
+      }
+      if (better(pp[s].kmax, pp[s].kidx, km, ki)) {
+        km = pp[s].kmax;
+        ki = pp[s].kidx;
+      }
+    }
+    double S = 0.0, E = 0.0;
+    for (int s = 0; s < a.splits; ++s) {
+      if (pp[s].lmax == -INFINITY) continue;
+      const double f2 = exp((double)pp[s].lmax - (double)M);
+      S += pp[s].S * f2;
+      E += (double)pp[s].E * f2;
+    }
+    E = E * 1.0001 + S * 1e-13;
+    const int tok = a.noisy ? ki : mi;
+    a.token[r] = tok;
+    a.conf[r] = (float)(1.0 / S);
+    sS[n] = S;
+    sE[n] = (float)E;
+    sM[n] = M;
+    sTok[n] = tok;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int bn = -1;
+    for (int n = 0; n < N; ++n) {
+      if (sS[n] < 0.0) continue;
+      if (bn < 0 || sS[n] < sS[bn]) bn = n;
+    }
+    best_n_s = bn;
+    if (bn >= 0) {
+      hi_s = sS[bn] + (double)sE[bn];
+      int c = 0;
+      for (int n = 0; n < N; ++n) {
+        if (sS[n] < 0.0) continue;
+        if (sS[n] - (double)sE[n] <= hi_s) sCand[c++] = n;
+      }
+      ncand_s = c;
+    } else {
+      ncand_s = 0;
+    }
+  }
+  __syncthreads();
+  int best = best_n_s;
+  if (ncand_s > 1) {
+    // re-decide exactly: S summed with fp64 exp in a fixed order
+    double bestS = 0.0;
+    best = -1;
+    for (int c = 0; c < ncand_s; ++c) {
+      const int n = sCand[c];
+      const int r = ws.rowmap[i * N + n];
+      const float* src = a.logits + (size_t)r * a.V;
+      const double M = (double)sM[n];
+      double s = 0.0;
+      for (int v = t; v < a.V; v += kThreads) s += exp((double)src[v] - M);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+      if (lane == 0) red[wave] = s;
+      __syncthreads();
+      double tot = 0.0;
+      for (int w = 0; w < kThreads / kWave; ++w) tot += red[w];
+      __syncthreads();
+      if (best < 0 || tot < bestS) {
+        best = n;
+        bestS = tot;
+      }
+    }
+  }
+  for (int n = t; n < N; n += kThreads) {
+    const int f = i * N + n;
+    a.next_state[f] = (n == best) ? sTok[n] : a.state[f];
+  }
+  if (t == 0) a.commit_pos[i] = best;
+}
+
+// ---------------------------------------------------------------------------
+// self-check of the fast-path bounds
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void atomic_max_pos_double(double* addr, double v) {
+  atomicMax((unsigned long long*)addr, (unsigned long long)__double_as_longlong(v));
+}
+
+__global__ __launch_bounds__(256) void selfcheck_gumbel_kernel(double* out) {
+  const uint64_t total = 1ull << 32;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  double worst = 0.0;
+  for (uint64_t w = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; w < total; w += stride) {
+    const double err = fabs((double)gumbel_fast((unsigned)w) - gumbel_exact_f64((unsigned)w));
+    worst = fmax(worst, err);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) worst = fmax(worst, __shfl_xor(worst, o, kWave));
+  if (threadIdx.x % kWave == 0) atomic_max_pos_double(out, worst);
+}
+
+__global__ __launch_bounds__(256) void selfcheck_exp2_kernel(double* out) {
+  // every fp32 x in [-126, 0]: bit patterns 0x80000000 .. 0xC2FC0000
+  const uint64_t first = 0x80000000ull, last = 0xC2FC0000ull;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  double worst = 0.0;
+  for (uint64_t b = first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b <= last; b += stride) {
+    const float x = __uint_as_float((unsigned)b);
+    const double ref = exp2((double)x);
+    const double err = fabs((double)fast_exp2(x) - ref) / ref;
+    worst = fmax(worst, err);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) worst = fmax(worst, __shfl_xor(worst, o, kWave));
+  if (threadIdx.x % kWave == 0) atomic_max_pos_double(out + 1, worst);
+}
+
+__global__ void zero2_kernel(double* out) {
+  if (threadIdx.x < 2) out[threadIdx.x] = 0.0;
+}
+
+}  // namespace
+
+CommitPlan commit_plan(int B1, int N, int M, int V, int items_max, bool noisy) {
+  CommitPlan pl;
+  pl.items_max = items_max;
+  const int max_splits = (V + kPerIter - 1) / kPerIter;
+  const int base = items_max > 0 ? items_max : 1;
+  int splits = ((noisy ? 2048 : 1024) + base - 1) / base;
+  if (splits > max_splits) splits = max_splits;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  int chunk = (V + splits - 1) / splits;
+  chunk = (chunk + kPerIter - 1) / kPerIter * kPerIter;
+  splits = (V + chunk - 1) / chunk;
+  pl.splits = splits;
+  pl.chunk = chunk;
+  pl.ws_bytes = ws_bytes(B1, N, M, items_max, splits);
+  return pl;
+}
+
+hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t* count,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(masked_rows_kernel, dim3(1), dim3(1024), 0, stream, state, B1 * N, rows, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
+                         const TreeArgs& tree, int N, int V, float temperature, uint64_t seed,
+                         uint64_t step0, int64_t pos0, int32_t* next_state, int32_t* commit_pos,
+                         int32_t* token, float* conf, void* ws_base, const CommitPlan& plan,
+                         hipStream_t stream) {
+  const bool noisy = temperature > 0.f;
+  WsLayout ws = ws_layout(ws_base, tree.B1, N, M, plan.items_max);
+  hipLaunchKernelGGL(commit_plan_kernel, dim3(1), dim3(kThreads), 0, stream, rows, M, N, tree, noisy, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (M > 0) {
+    RowsArgs ra;
+    ra.logits = logits;
+    ra.rows = rows;
+    ra.M = M;
+    ra.N = N;
+    ra.V = V;
+    ra.splits = plan.splits;
+    ra.chunk = plan.chunk;
+    ra.inv_t = noisy ? 1.0f / temperature : 0.f;
+    ra.seed = seed;
+    ra.step0 = step0;
+    ra.pos0 = (uint64_t)pos0;
+    const unsigned blocks = (unsigned)plan.items_max * plan.splits;
+    if (noisy)
+      hipLaunchKernelGGL((commit_rows_kernel<true, kItemRows>), dim3(blocks), dim3(kThreads), 0, stream, ra, ws);
+    else
+      hipLaunchKernelGGL((commit_rows_kernel<false, 1>), dim3(blocks), dim3(kThreads), 0, stream, ra, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  FinArgs fa;
+  fa.logits = logits;
+  fa.state = state;
+  fa.next_state = next_state;
+  fa.commit_pos = commit_pos;
+  fa.token = token;
+  fa.conf = conf;
+  fa.N = N;
+  fa.V = V;
+  fa.splits = plan.splits;
+  fa.noisy = noisy;
+  hipLaunchKernelGGL(commit_finalize_kernel, dim3(tree.B1), dim3(kThreads), 0, stream, fa, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_selfcheck(double* out, hipStream_t stream) {
+  hipLaunchKernelGGL(zero2_kernel, dim3(1), dim3(64), 0, stream, out);
+  hipLaunchKernelGGL(selfcheck_gumbel_kernel, dim3(4096), dim3(256), 0, stream, out);
+  hipLaunchKernelGGL(selfcheck_exp2_kernel, dim3(4096), dim3(256), 0, stream, out);
+  return hipGetLastError();
+}
+
+}  // namespace sfv

@@ -1,0 +1,60 @@
+// Device helpers shared by the libsfv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Workgroup ids are dealt to the XCDs round-robin (id % 8).  This returns a
+// logical id such that consecutive logical ids run on the same XCD, so tiles
+// that share data (and so L2 lines) can be given consecutive logical ids.
+__device__ __forceinline__ int xcd_logical_block(int b, int total) {
+  const int xcd = b % kXcds;
+  const int slot = b / kXcds;
+  const int per = total / kXcds;
+  const int extra = total % kXcds;
+  return xcd * per + (xcd < extra ? xcd : extra) + slot;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
+  return __uint_as_float(((unsigned)h) << 16);
+}
+
+// fp32 -> bf16 round to nearest even (inputs are finite).
+__device__ __forceinline__ unsigned short float_to_bf16_bits(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return (unsigned)float_to_bf16_bits(lo) | ((unsigned)float_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+}  // namespace sfv

@@ -1,0 +1,67 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sfv {
+
+struct AttnPlan {
+  int rows_total;  // B1 * N * G query rows per kv head
+  int row_tiles;   // ceil(rows_total / 128)
+  int splits;      // context key ranges
+  int chunk;       // context keys per range (multiple of 64)
+  size_t ws_bytes;
+};
+
+AttnPlan attn_plan(int B1, int N, int L, int Hq, int Hkv, int d);
+
+hipError_t launch_attention(const void* q, const void* k_blk, const void* v_blk,
+                            const void* k_ctx, const void* v_ctx, int B1, int N, int L,
+                            int Hq, int Hkv, int d, float scale, void* o, float* lse,
+                            void* ws, const AttnPlan& plan, hipStream_t stream);
+
+hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows,
+                              int32_t* count, hipStream_t stream);
+
+hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R, const void* w,
+                          int D, int V, float* logits, hipStream_t stream);
+
+constexpr int kMaxBranches = 64;
+constexpr int kMaxBlock = 256;
+
+struct CommitPlan {
+  int splits;        // vocabulary ranges per row
+  int chunk;         // vocab ids per range (multiple of 2048)
+  int items_max;     // upper bound of work items (rows, or row groups at T > 0)
+  size_t ws_bytes;
+};
+
+// Tree description passed by value to the kernels.
+struct TreeArgs {
+  int B1;
+  int levels;
+  signed char depth[kMaxBranches];
+  signed char parent[kMaxBranches];
+  unsigned char by_level[kMaxBranches];    // branches sorted by depth
+  unsigned char level_start[kMaxBranches + 1];
+};
+
+// Rows of equal (depth, position) share one noise sweep at T > 0, up to 8 per item.
+constexpr int kItemRowsHost = 8;
+CommitPlan commit_plan(int B1, int N, int M, int V, int items_max, bool noisy);
+
+hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
+                         const TreeArgs& tree, int N, int V, float temperature, uint64_t seed,
+                         uint64_t step0, int64_t pos0, int32_t* next_state, int32_t* commit_pos,
+                         int32_t* token, float* conf, void* ws, const CommitPlan& plan,
+                         hipStream_t stream);
+
+hipError_t launch_match(const int32_t* state, const int32_t* next_state, const int32_t* commit_pos,
+                        const TreeArgs& tree, int N, int k_max, int S_max, int32_t* chain,
+                        int32_t* n_accepted, int32_t* status, hipStream_t stream);
+
+hipError_t launch_selfcheck(double* out, hipStream_t stream);
+
+}  // namespace sfv

@@ -1,0 +1,108 @@
+"""One verification step on the GPU through the C ABI.
+
+PyTorch provides device memory and the stream; the five calls below do all of
+the work in libsfv's kernels: shared-prefix attention, masked-row scan, LM head
+over the masked rows, commit, and the draft-tree match.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import sfv
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Host inputs from synth.draw_inputs -> device tensors (bf16 stays bf16)."""
+    out = {}
+    for k, v in inp.items():
+        if k == "parent":
+            out[k] = np.asarray(v, dtype=np.int32)
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        if v.dtype == np.uint16:
+            t = t.view(torch.bfloat16)
+        out[k] = t.to(device)
+    return out
+
+
+class VerifyStep:
+    """Buffers and calls of one multi-branch verification step of fixed shape."""
+
+    def __init__(self, B1, N, L, Hq, Hkv, d, D, V, M, parent, temperature, seed, step0, pos0,
+                 S_max=-1, device="cuda"):
+        sfv.load()
+        self.B1, self.N, self.L, self.Hq, self.Hkv, self.d = B1, N, L, Hq, Hkv, d
+        self.D, self.V, self.M = D, V, M
+        self.parent = [int(x) for x in parent]
+        self.T, self.seed, self.step0, self.pos0 = float(temperature), seed, step0, pos0
+        self.S_max = S_max
+        self.scale = 1.0 / math.sqrt(d)
+        dev = device
+        self.o = torch.empty((B1, N, Hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B1, N, Hq), dtype=torch.float32, device=dev)
+        self.attn_ws_bytes = sfv.sfv_attend_workspace_bytes(B1, N, L, Hq, Hkv, d)
+        self.attn_ws = torch.empty(max(1, self.attn_ws_bytes), dtype=torch.uint8, device=dev)
+        self.rows = torch.zeros(B1 * N, dtype=torch.int32, device=dev)
+        self.count = torch.empty(1, dtype=torch.int32, device=dev)
+        self.logits = torch.empty((max(1, M), V), dtype=torch.float32, device=dev)
+        self.commit_ws_bytes = sfv.sfv_commit_workspace_bytes(B1, N, M, V)
+        self.commit_ws = torch.empty(max(1, self.commit_ws_bytes), dtype=torch.uint8, device=dev)
+        self.next_state = torch.empty((B1, N), dtype=torch.int32, device=dev)
+        self.commit_pos = torch.empty((B1, 1), dtype=torch.int32, device=dev)
+        self.token = torch.empty(max(1, M), dtype=torch.int32, device=dev)
+        self.conf = torch.empty(max(1, M), dtype=torch.float32, device=dev)
+        self.chain = torch.empty(B1, dtype=torch.int32, device=dev)
+        self.n_accepted = torch.empty(1, dtype=torch.int32, device=dev)
+        self.status = torch.empty(1, dtype=torch.int32, device=dev)
+
+    # the individual rows of the hot path -----------------------------------
+    def attend(self, x, stream=None):
+        sfv.sfv_attend_branches(x["q"], x["k_blk"], x["v_blk"], x["k_ctx"], x["v_ctx"], self.B1,
+                                self.N, self.L, self.Hq, self.Hkv, self.d, self.scale, self.o,
+                                self.lse, self.attn_ws, self.attn_ws_bytes, stream)
+
+    def masked_rows(self, x, stream=None):
+        sfv.sfv_masked_rows(x["state"], self.B1, self.N, self.rows, self.count, stream)
+
+    def lm_head(self, x, stream=None):
+        sfv.sfv_lm_head(x["hidden"], self.rows, self.M, self.B1 * self.N, x["w"], self.D, self.V,
+                        self.logits, stream)
+
+    def commit(self, x, logits=None, stream=None):
+        sfv.sfv_commit(self.logits if logits is None else logits, self.rows, self.M, x["state"],
+                       self.parent, self.B1, self.N, self.V, self.T, self.seed, self.step0,
+                       self.pos0, 1, 0.0, self.next_state, self.commit_pos, self.token, self.conf,
+                       self.commit_ws, self.commit_ws_bytes, stream)
+
+    def match(self, x, stream=None):
+        sfv.sfv_match_tree(x["state"], self.next_state, self.commit_pos, self.parent, self.B1,
+                           self.N, 1, self.S_max, self.chain, self.n_accepted, self.status, stream)
+
+    def run(self, x, stream=None):
+        """The whole hot path, stream-ordered, no host synchronisation."""
+        self.attend(x, stream)
+        self.masked_rows(x, stream)
+        self.lm_head(x, stream)
+        self.commit(x, stream=stream)
+        self.match(x, stream)
+
+    def results(self) -> dict:
+        torch.cuda.synchronize()
+        M = self.M
+        return dict(
+            o=self.o, lse=self.lse, rows=self.rows[:M].cpu().numpy(), count=int(self.count.item()),
+            logits=self.logits[:M], next_state=self.next_state.cpu().numpy(),
+            commit_pos=self.commit_pos.cpu().numpy(), token=self.token[:M].cpu().numpy(),
+            conf=self.conf[:M].cpu().numpy(), chain=self.chain.cpu().numpy(),
+            h=int(self.n_accepted.item()), status=int(self.status.item()))
+
+
+def step_for(wl, inp: dict, device="cuda", S_max=None) -> VerifyStep:
+    from .synth import masked_count
+    M = masked_count(inp["state"])
+    return VerifyStep(wl.B1, wl.N, wl.L, wl.Hq, wl.Hkv, wl.d, wl.D, wl.V, M, inp["parent"], wl.T,
+                      wl.seed, wl.step0, wl.pos0, S_max=wl.S_t if S_max is None else S_max,
+                      device=device)

@@ -1,0 +1,176 @@
+/*
+ * sfv.h — C ABI of libsfv: one multi-branch draft-verification step of
+ * speculative decoding for masked diffusion language models, on one MI355X
+ * (gfx950).
+ *
+ * The step (SpecFold: "Folding Multi-Branch Redundancy for Faster Speculative
+ * Decoding in Diffusion Language Models", introduction and Fig. 1-(b); "On the
+ * SPOT: Enhancing Speculative Decoding for Diffusion Language Models via
+ * Commit-Order Prediction", coupled-noise match and Propositions 1-2):
+ *   B1 = B + 1 block states of length N — the main branch (index 0) and B
+ *   drafts whose parents have smaller indices — are verified in one batched
+ *   pass against a shared cached context of L positions, then the target's
+ *   own commit is taken on every branch and the main branch's next state is
+ *   matched against the drafted states.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers unless their name ends in _host.
+ *     bf16 tensors are passed as const void* holding IEEE bfloat16 bits.
+ *     All tensors are dense, row-major, in the layout given beside them.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is launched and the return value says why
+ *     (sfv_last_error() gives a message).  On success the work is enqueued
+ *     on `stream` (a hipStream_t passed as void*; NULL = the null stream)
+ *     and the call returns at once; outputs are valid after the stream is
+ *     synchronised.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no state between calls; calls on distinct streams with
+ *     distinct outputs and workspaces may overlap.
+ *   - The mask token is SFV_MASK (-1); tokens lie in [0, V).
+ */
+#ifndef SFV_H
+#define SFV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SFV_OK = 0,
+  SFV_E_INVAL = -1,        /* null pointer, size out of range */
+  SFV_E_UNSUPPORTED = -2,  /* valid but not implemented (head dim, group size, ...) */
+  SFV_E_TREE = -3,         /* parent_host[0] != -1 or parent_host[i] not in [0, i) */
+  SFV_E_STATE = -4,        /* device-detected: a draft does not extend its parent */
+  SFV_E_WORKSPACE = -5,    /* workspace smaller than the *_workspace_bytes size */
+  SFV_E_HIP = -6           /* a HIP launch failed */
+};
+
+#define SFV_MASK (-1)
+#define SFV_MAX_BRANCHES 64  /* B1 limit: the tree is host control data */
+#define SFV_MAX_BLOCK 256    /* N limit */
+
+/* Message of the last non-OK return on this thread ("" if none). */
+const char* sfv_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sfv_version(void);
+
+/*
+ * Shared-prefix attention of every branch.
+ * SpecFold, introduction (bidirectional in-block attention; the shared-prefix
+ * KV cache reused across all branches) and App. A.1 (streaming-softmax state
+ * (m, Z, O) over the concatenated prefix and block keys).
+ *
+ * For every branch i, position n and query head h, with kv head g = h / (Hq/Hkv):
+ *   keys = the L context keys of head g followed by the N block keys of
+ *   branch i, head g; no key is masked (bidirectional block).
+ *   s_j = softmax_scale * <q, k_j>;  o = sum_j e^{s_j} v_j / sum_j e^{s_j};
+ *   lse = ln sum_j e^{s_j}  (natural log).
+ *
+ *   q      [B1][N][Hq][d]  bf16      k_blk, v_blk [B1][N][Hkv][d] bf16
+ *   k_ctx, v_ctx [Hkv][L][d] bf16 — one copy shared by all branches
+ *   o      [B1][N][Hq][d]  bf16 (round to nearest even)
+ *   lse    [B1][N][Hq]     fp32
+ * Supported: d in {32, 64, 128}; Hq/Hkv in {1, 2, 4, 8}; 1 <= B1 <= 64;
+ * 1 <= N <= 256; L >= 0.  fp32 accumulation.
+ * `workspace` holds split-context partial states; its size comes from
+ * sfv_attend_workspace_bytes (may be 0, then workspace may be NULL).
+ */
+int sfv_attend_workspace_bytes(int B1, int N, int L, int Hq, int Hkv, int d, size_t* bytes);
+int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk,
+                        const void* k_ctx, const void* v_ctx,
+                        int B1, int N, int L, int Hq, int Hkv, int d, float softmax_scale,
+                        void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Masked-row list.  SpecFold, introduction: the forward map returns token
+ * distributions for the masked positions of the active block.
+ *   state [B1][N] int32 (SFV_MASK = masked)
+ *   rows  [B1*N] int32 out: flat ids i*N + n of masked positions in (i, n)
+ *         order, the first *count entries valid
+ *   count [1] int32 out
+ */
+int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t* count,
+                    void* stream);
+
+/*
+ * LM head over the masked rows.  SpecFold, Appendix B (the language-model
+ * head is a plain dense product): logits[r][v] = sum_k hidden[rows[r]][k] * w[v][k].
+ *   hidden [R][D] bf16 (R = B1*N, rows index it); rows [M] int32, each in [0, R)
+ *   w      [V][D] bf16;  logits [M][V] fp32 (fp32 accumulation)
+ * Supported: D % 64 == 0, 1 <= V, 0 <= M.  Row ids are not range-checked on
+ * the device: the caller guarantees 0 <= rows[r] < R.
+ */
+int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R,
+                const void* w, int D, int V, float* logits, void* stream);
+
+/*
+ * Commit of every branch: token per masked row, confidence, unmask-argmax.
+ * SPOT, "Important context" (exact decoding commits one position per pass;
+ * coupled-noise match) and Proposition 2; SpecFold, introduction (an
+ * unmasking rule picks high-confidence masked positions).
+ *
+ * For masked row r = (i, n) with fp32 logits l:
+ *   T == 0: token = lowest v attaining max l.
+ *   T  > 0: invT = fl32(1/T); g_v = fl32(-ln(-ln u_v)), u_v = (w_v + 1/2) 2^-32,
+ *           w_v the 32-bit Philox4x64-10 word for (seed, step0 + depth(i),
+ *           pos0 + n, v) (key (seed, 0), counter (v>>3, pos, step, 0), word
+ *           (v&7)>>1, low half for even v); key_v = fl32(fl32(l_v*invT) + g_v);
+ *           token = lowest v attaining max key.  Branches at equal depth share
+ *           the noise of a position.
+ *   S = sum_v exp(l_v - max l) (fp64 decision); conf = fl32(1/S) (fp32 fast
+ *   path, relative error below 1e-5).
+ * Per branch: the masked position with the smallest S (ties: lowest n) is
+ * committed: next_state[i][n*] = token; commit_pos[i][0] = n*, or -1 when the
+ * branch has no masked position.  k_max must be 1 (tau is ignored).
+ *
+ *   logits [M][V] fp32; rows [M] int32 = sfv_masked_rows(state) order
+ *   state, next_state [B1][N] int32; parent_host [B1] host int32, parent[0] = -1
+ *   commit_pos [B1][k_max] int32; token [M] int32; conf [M] fp32
+ *   workspace: sfv_commit_workspace_bytes(B1, N, M, V) bytes
+ * Supported: V % 8 == 0, V < 2^31 / 8, T >= 0 and finite.
+ */
+int sfv_commit_workspace_bytes(int B1, int N, int M, int V, size_t* bytes);
+int sfv_commit(const float* logits, const int32_t* rows, int M,
+               const int32_t* state, const int32_t* parent_host,
+               int B1, int N, int V, float temperature,
+               uint64_t seed, uint64_t step0, int64_t pos0, int k_max, float tau,
+               int32_t* next_state, int32_t* commit_pos, int32_t* token, float* conf,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * State-equality walk over the draft tree.  SpecFold, introduction (a later
+ * main-branch state equal to a cached draft reuses its logits); SPOT, "How
+ * does SPOT draft and verify?" (accept the longest prefix consistent with the
+ * target's own trajectory).
+ *
+ * cur = 0; repeat at most B1-1 times: stop if commit_pos[cur][0] == -1;
+ * j = lowest draft index >= 1 with state[j] == next_state[cur] (64-bit state
+ * hash, confirmed by full comparison); stop if none; append j; cur = j.
+ *   chain [B1] int32 out (-1 padded); n_accepted [1] int32 out (h)
+ *   status [1] int32 out: SFV_OK, or SFV_E_STATE when S_max >= 0 and some
+ *   draft changes or re-masks a parent position or unmasks more than S_max
+ *   positions over its parent (then h = 0).  S_max < 0 skips that check.
+ * A miss is not an error: h = 0.
+ */
+int sfv_match_tree(const int32_t* state, const int32_t* next_state, const int32_t* commit_pos,
+                   const int32_t* parent_host, int B1, int N, int k_max, int S_max,
+                   int32_t* chain, int32_t* n_accepted, int32_t* status, void* stream);
+
+/*
+ * Device self-check of the fast-path error bounds the commit relies on.
+ * Sweeps every 32-bit noise word and every fp32 argument in [-126, 0] of the
+ * fast exp2 and writes out[0] = max |g_fast - g_exact| over all words and
+ * out[1] = max relative error of the fast exp2 (fp64 reference on the device).
+ *   out [2] fp64 device.  Synchronous on `stream`'s work only.
+ */
+int sfv_selfcheck_bounds(double* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFV_H */

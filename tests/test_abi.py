@@ -1,0 +1,144 @@
+"""The C ABI on the host: the library loads without a GPU, exports every
+entry point include/sfv.h declares, and rejects bad arguments synchronously
+(each check runs before anything is enqueued, so no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from branch_verify_amd import sfv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sfv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sfv.LIB_PATH):
+        pytest.fail("libsfv.so is not built (run __graft_entry__.build())")
+    return sfv.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sfv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(sfv.EXPORTS)
+
+
+def test_version_and_empty_error(lib):
+    assert lib.sfv_version() >= 100
+
+
+def _ws(fn, *args):
+    out = ctypes.c_size_t(0)
+    return fn(*args, ctypes.byref(out)), out.value
+
+
+def test_attend_workspace_validation(lib):
+    assert _ws(lib.sfv_attend_workspace_bytes, 3, 8, 64, 4, 2, 32)[0] == sfv.SFV_OK
+    assert _ws(lib.sfv_attend_workspace_bytes, 0, 8, 64, 4, 2, 32)[0] == sfv.SFV_E_INVAL
+    assert _ws(lib.sfv_attend_workspace_bytes, 65, 8, 64, 4, 2, 32)[0] == sfv.SFV_E_INVAL
+    assert _ws(lib.sfv_attend_workspace_bytes, 3, 257, 64, 4, 2, 32)[0] == sfv.SFV_E_INVAL
+    assert _ws(lib.sfv_attend_workspace_bytes, 3, 8, -1, 4, 2, 32)[0] == sfv.SFV_E_INVAL
+    assert _ws(lib.sfv_attend_workspace_bytes, 3, 8, 64, 6, 4, 32)[0] == sfv.SFV_E_INVAL
+    assert _ws(lib.sfv_attend_workspace_bytes, 3, 8, 64, 48, 3, 32)[0] == sfv.SFV_E_UNSUPPORTED
+    assert _ws(lib.sfv_attend_workspace_bytes, 3, 8, 64, 4, 2, 96)[0] == sfv.SFV_E_UNSUPPORTED
+    assert b"96" in lib.sfv_last_error()
+    assert lib.sfv_attend_workspace_bytes(3, 8, 64, 4, 2, 32, None) == sfv.SFV_E_INVAL
+
+
+def test_attend_rejects_before_launch(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    args = [fake] * 5 + [3, 8, 64, 4, 2, 32, ctypes.c_float(0.17), fake, fake]
+    # null q
+    assert lib.sfv_attend_branches(None, *args[1:], None, 0, None) == sfv.SFV_E_INVAL
+    # misaligned output
+    bad = list(args); bad[12] = P(0x1002)   # o
+    rc, need = _ws(lib.sfv_attend_workspace_bytes, 3, 8, 64, 4, 2, 32)
+    assert lib.sfv_attend_branches(*bad, fake, need, None) == sfv.SFV_E_INVAL
+    # workspace too small when splits are needed
+    rc, need = _ws(lib.sfv_attend_workspace_bytes, 9, 32, 4096, 32, 8, 128)
+    assert need > 0
+    args2 = [fake] * 5 + [9, 32, 4096, 32, 8, 128, ctypes.c_float(0.088), fake, fake]
+    assert lib.sfv_attend_branches(*args2, fake, need - 1, None) == sfv.SFV_E_WORKSPACE
+    # non-finite scale
+    args3 = list(args); args3[11] = ctypes.c_float(float("inf"))
+    assert lib.sfv_attend_branches(*args3, fake, 1 << 30, None) == sfv.SFV_E_INVAL
+
+
+def test_lm_head_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    assert lib.sfv_lm_head(f, f, -1, 8, f, 128, 512, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head(f, f, 4, 8, f, 100, 512, f, None) == sfv.SFV_E_UNSUPPORTED
+    assert lib.sfv_lm_head(None, f, 4, 8, f, 128, 512, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head(f, f, 4, 0, f, 128, 512, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head(P(0x1004), f, 4, 8, f, 128, 512, f, None) == sfv.SFV_E_INVAL
+
+
+def _commit(lib, parent, B1=3, N=8, M=4, V=512, T=0.0, k_max=1, ws_bytes=None, logits=0x1000):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    par = (ctypes.c_int32 * len(parent))(*parent)
+    if ws_bytes is None:
+        ws_bytes = 1 << 30
+    return lib.sfv_commit(P(logits), f, M, f, ctypes.cast(par, P), B1, N, V, ctypes.c_float(T),
+                          ctypes.c_uint64(1), ctypes.c_uint64(2), ctypes.c_int64(3), k_max,
+                          ctypes.c_float(0.0), f, f, f, f, f, ws_bytes, None)
+
+
+def test_commit_validation(lib):
+    assert _commit(lib, [0, 0, 1]) == sfv.SFV_E_TREE
+    assert _commit(lib, [-1, 1, 0]) == sfv.SFV_E_TREE
+    assert _commit(lib, [-1, 0, 3]) == sfv.SFV_E_TREE
+    assert _commit(lib, [-1, 0, 1], M=25) == sfv.SFV_E_INVAL
+    assert _commit(lib, [-1, 0, 1], V=500) == sfv.SFV_E_UNSUPPORTED
+    assert _commit(lib, [-1, 0, 1], T=-1.0) == sfv.SFV_E_INVAL
+    assert _commit(lib, [-1, 0, 1], T=float("nan")) == sfv.SFV_E_INVAL
+    assert _commit(lib, [-1, 0, 1], k_max=0) == sfv.SFV_E_INVAL
+    assert _commit(lib, [-1, 0, 1], k_max=2) == sfv.SFV_E_UNSUPPORTED
+    assert _commit(lib, [-1, 0, 1], ws_bytes=16) == sfv.SFV_E_WORKSPACE
+    assert _commit(lib, [-1, 0, 1], logits=0x1004) == sfv.SFV_E_INVAL
+    assert _commit(lib, [-1] + [0] * 64, B1=65) == sfv.SFV_E_INVAL
+
+
+def test_commit_workspace_covers_every_tree(lib):
+    for (B1, N, M, V) in [(3, 8, 10, 512), (9, 32, 144, 151936), (33, 64, 1478, 151936), (64, 256, 16384, 8)]:
+        rc, need = _ws(lib.sfv_commit_workspace_bytes, B1, N, M, V)
+        assert rc == sfv.SFV_OK and need > 0
+    assert _ws(lib.sfv_commit_workspace_bytes, 3, 8, 30, 512)[0] == sfv.SFV_E_INVAL
+
+
+def test_match_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    par = (ctypes.c_int32 * 3)(-1, 0, 2)
+    assert lib.sfv_match_tree(f, f, f, ctypes.cast(par, P), 3, 8, 1, 2, f, f, f, None) == sfv.SFV_E_TREE
+    par = (ctypes.c_int32 * 3)(-1, 0, 1)
+    assert lib.sfv_match_tree(f, f, f, ctypes.cast(par, P), 3, 0, 1, 2, f, f, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_match_tree(None, f, f, ctypes.cast(par, P), 3, 8, 1, 2, f, f, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_match_tree(f, f, f, None, 3, 8, 1, 2, f, f, f, None) == sfv.SFV_E_INVAL
+
+
+def test_masked_rows_validation(lib):
+    f = ctypes.c_void_p(0x1000)
+    assert lib.sfv_masked_rows(None, 3, 8, f, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_masked_rows(f, 0, 8, f, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_masked_rows(f, 3, 300, f, f, None) == sfv.SFV_E_INVAL
+
+
+def test_single_hip_runtime_in_process(lib):
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) <= 1, libs

@@ -1,0 +1,372 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Acceptance (same seeded inputs on both sides):
+  * commit and match: tokens, committed positions, next states and matched
+    draft indices bit-exact given the same fp32 logits;
+  * attention: O within 2e-2 max-abs (bf16 in, fp32 accumulation), LSE within
+    1e-5 relative;
+  * LM-head logits within 3e-2 max-abs.
+Sizes the oracle finishes in seconds are compared element by element; the
+full workloads are compared on sampled outputs the oracle computes one by one,
+in the launch configuration the benchmark times.  Every GPU call is run twice
+and must be bit-identical (no atomics feed any decision)."""
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from branch_verify_amd import synth
+from branch_verify_amd.step import VerifyStep, step_for, to_device
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+ATT_ABS = 2e-2
+LSE_REL = 1e-5
+LOGIT_ABS = 3e-2
+f32 = synth.bf16_bits_to_f32
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=1)
+def host_inputs(idx):
+    return synth.draw_inputs(synth.WORKLOADS[idx])
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def oracle_attention_rows(x, samples, scale):
+    """Oracle O and LSE for sampled (i, n, h), one row at a time."""
+    q, kb, vb, kc, vc = (f32(x[k]) for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx"))
+    G = q.shape[2] // kb.shape[2]
+    outs, lses = [], []
+    for (i, n, h) in samples:
+        g = h // G
+        o, l = O.attention(q[i:i + 1, n:n + 1, h:h + 1], kb[i:i + 1, :, g:g + 1],
+                           vb[i:i + 1, :, g:g + 1], kc[g:g + 1], vc[g:g + 1], scale)
+        outs.append(o[0, 0, 0])
+        lses.append(l[0, 0, 0])
+    return np.array(outs), np.array(lses)
+
+
+def check_attention(x, step, full):
+    o_gpu = step.o.float().cpu().numpy()
+    lse_gpu = step.lse.cpu().numpy()
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu))
+    if full:
+        o_ref, lse_ref = O.attention(*(f32(x[k]) for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx")),
+                                     step.scale)
+        err_o = np.max(np.abs(o_gpu - o_ref))
+        err_l = np.max(np.abs(lse_gpu - lse_ref) / np.abs(lse_ref))
+    else:
+        rng = np.random.default_rng(0)
+        B1, N, Hq = lse_gpu.shape
+        samples = [(int(rng.integers(B1)), int(rng.integers(N)), int(rng.integers(Hq))) for _ in range(192)]
+        samples += [(0, 0, 0), (B1 - 1, N - 1, Hq - 1), (B1 - 1, 0, Hq // 2)]
+        o_ref, lse_ref = oracle_attention_rows(x, samples, step.scale)
+        og = np.array([o_gpu[s] for s in samples])
+        lg = np.array([lse_gpu[s] for s in samples])
+        err_o = np.max(np.abs(og - o_ref))
+        err_l = np.max(np.abs(lg - lse_ref) / np.abs(lse_ref))
+    say(f"attention max|dO|={err_o:.3e} max rel dLSE={err_l:.3e}")
+    assert err_o <= ATT_ABS
+    assert err_l <= LSE_REL
+
+
+# ---------------------------------------------------------------------------
+# LM head
+# ---------------------------------------------------------------------------
+def check_lm_head(x, res, full):
+    rows = res["rows"]
+    logits = res["logits"]
+    M, V = logits.shape
+    hidden = f32(x["hidden"])
+    if full:
+        ref = O.lm_head(hidden, rows, f32(x["w"]))
+        got = logits.cpu().numpy()
+        err = np.max(np.abs(got - ref))
+    else:
+        rng = np.random.default_rng(1)
+        rsel = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 14)]))
+        cols = np.unique(np.concatenate([np.arange(256), np.arange(V - 256, V),
+                                         rng.integers(0, V, 4096),
+                                         np.arange(127, V, 128)[:64], np.arange(128, V, 128)[-64:]]))
+        w = f32(x["w"][cols])
+        ref = hidden[rows[rsel]].astype(np.float64) @ w.astype(np.float64).T
+        got = logits[torch.from_numpy(rsel).to(logits.device)][:, torch.from_numpy(cols).to(logits.device)]
+        err = np.max(np.abs(got.cpu().numpy() - ref))
+    say(f"lm_head max|dlogit|={err:.3e}")
+    assert err <= LOGIT_ABS
+
+
+# ---------------------------------------------------------------------------
+# commit and match
+# ---------------------------------------------------------------------------
+def check_commit_match(x, res, wl_T, seed, step0, pos0, S_max, logits_host=None):
+    rows = res["rows"]
+    lg = res["logits"].cpu().numpy() if logits_host is None else logits_host
+    nxt, cpos, tok, conf, S = O.commit(lg, rows, x["state"], x["parent"], wl_T, seed, step0, pos0)
+    assert np.array_equal(res["token"], tok), np.flatnonzero(res["token"] != tok)[:10]
+    assert np.array_equal(res["commit_pos"][:, 0], cpos[:, 0])
+    assert np.array_equal(res["next_state"], nxt)
+    rel = np.max(np.abs(res["conf"].astype(np.float64) - conf.astype(np.float64)) / conf) if conf.size else 0.0
+    say(f"commit tokens/positions exact; conf max rel err {rel:.2e}")
+    assert rel <= 1e-5
+    chain, h, status = O.match_tree(x["state"], nxt, cpos, x["parent"], S_max)
+    assert res["status"] == status
+    assert res["h"] == h
+    assert np.array_equal(res["chain"], chain)
+    return h
+
+
+def run_twice(step, xd):
+    step.run(xd)
+    first = step.results()
+    snap = {k: (v.clone() if torch.is_tensor(v) else np.copy(v) if isinstance(v, np.ndarray) else v)
+            for k, v in first.items()}
+    step.run(xd)
+    second = step.results()
+    for k in snap:
+        a, b = snap[k], second[k]
+        if torch.is_tensor(a):
+            assert torch.equal(a, b), f"{k} differs between two identical runs"
+        elif isinstance(a, np.ndarray):
+            assert np.array_equal(a, b), f"{k} differs between two identical runs"
+        else:
+            assert a == b, k
+    return second
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_full_step_parity(gpu_lib, idx):
+    wl = synth.WORKLOADS[idx]
+    say(f"workload {idx} {wl.name}: drawing inputs")
+    x = host_inputs(idx)
+    xd = to_device(x)
+    step = step_for(wl, x)
+    say(f"workload {idx}: B1={wl.B1} N={wl.N} L={wl.L} M={step.M} running the step twice")
+    res = run_twice(step, xd)
+    assert res["count"] == step.M
+    assert np.array_equal(res["rows"], O.masked_rows(x["state"]))
+    check_attention(x, step, full=idx <= 4)
+    check_lm_head(x, res, full=idx == 1)
+    check_commit_match(x, res, wl.T, wl.seed, wl.step0, wl.pos0, wl.S_t)
+    del xd, step
+    torch.cuda.empty_cache()
+
+
+def test_selfcheck_bounds(gpu_lib):
+    out = torch.zeros(2, dtype=torch.float64, device="cuda")
+    say("self-check: all 2^32 noise words and all fp32 exp2 arguments in [-126, 0]")
+    gpu_lib.sfv_selfcheck_bounds(out)
+    torch.cuda.synchronize()
+    g_err, e_rel = out.cpu().tolist()
+    say(f"max |g_fast - g| = {g_err:.3e}; max rel err exp2 = {e_rel:.3e}")
+    assert g_err < (1.0 / 4096) / 4          # commit margin uses 1/4096
+    assert e_rel < 2.0 ** -22                # commit error model uses 2^-20
+
+
+# ---------------------------------------------------------------------------
+# commit + match on planted trees (toy target; SPOT Propositions 1-2)
+# ---------------------------------------------------------------------------
+def _planted_case(rng, N, V, T, step0, pos0, seed, depth, decoys):
+    s0 = rng.integers(0, V, N).astype(np.int32)
+    s0[rng.choice(N, max(depth + 2, N // 2), replace=False)] = O.MASK
+    traj = [s0]
+    for t in range(depth):
+        cur = traj[-1][None]
+        rows = O.masked_rows(cur)
+        lg = synth.state_keyed_logits(seed, cur[0], V)[rows]
+        nxt, *_ = O.commit(lg, rows, cur, np.array([-1]), T, seed, step0 + t, pos0)
+        traj.append(nxt[0])
+    states, parent = [traj[0]], [-1]
+    for t in range(1, len(traj)):
+        parent.append(len(states) - 1)
+        states.append(traj[t])
+    for _ in range(decoys):
+        p = int(rng.integers(0, len(states)))
+        row = states[p].copy()
+        free = np.flatnonzero(row == O.MASK)
+        if free.size == 0:
+            continue
+        row[int(rng.choice(free))] = int(rng.integers(0, V))
+        if any(np.array_equal(row, s) for s in traj):
+            continue
+        states.append(row)
+        parent.append(p)
+    st = np.stack(states).astype(np.int32)
+    return st, np.array(parent, dtype=np.int32), len(traj) - 1
+
+
+def _run_commit_match(st, parent, V, T, seed, step0, pos0, logits_host, S_max=1):
+    B1, N = st.shape
+    rows = O.masked_rows(st)
+    M = rows.size
+    step = VerifyStep(B1, N, 0, 1, 1, 32, 64, V, M, parent, T, seed, step0, pos0, S_max=S_max)
+    xd = {"state": torch.from_numpy(st).cuda()}
+    step.masked_rows(xd)
+    lg = torch.from_numpy(np.ascontiguousarray(logits_host)).cuda()
+    step.commit(xd, logits=lg)
+    step.match(xd)
+    torch.cuda.synchronize()
+    res = dict(rows=step.rows[:M].cpu().numpy(), logits=lg, token=step.token[:M].cpu().numpy(),
+               conf=step.conf[:M].cpu().numpy(), commit_pos=step.commit_pos.cpu().numpy(),
+               next_state=step.next_state.cpu().numpy(), chain=step.chain.cpu().numpy(),
+               h=int(step.n_accepted.item()), status=int(step.status.item()))
+    return res
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0, 0.7])
+@pytest.mark.parametrize("case", range(4))
+def test_planted_chain_match(gpu_lib, T, case):
+    rng = np.random.default_rng(300 + case)
+    N, V, seed = [8, 32, 16, 64][case], [512, 151936, 4096, 2048][case], 77 + case
+    step0, pos0 = 900 + case, 4096
+    depth = int(rng.integers(1, 6))
+    st, parent, planted = _planted_case(rng, N, V, T, step0, pos0, seed, depth, decoys=int(rng.integers(3, 20)))
+    say(f"planted case {case} T={T} B1={st.shape[0]} N={N} V={V} depth={depth}")
+    rows = O.masked_rows(st)
+    lg = np.stack([synth.state_keyed_logits(seed, st[r // N], V)[r % N] for r in rows])
+    res = _run_commit_match(st, parent, V, T, seed, step0, pos0, lg)
+    x = dict(state=st, parent=parent)
+    h = check_commit_match(x, res, T, seed, step0, pos0, 1, logits_host=lg)
+    assert h == planted
+
+
+def test_tie_breaks(gpu_lib):
+    V, N = 2048, 6
+    rng = np.random.default_rng(5)
+    st = np.array([[-1, -1, -1, 4, -1, 9],
+                   [7, -1, -1, 4, -1, 9],
+                   [7, -1, -1, 4, -1, 9],      # duplicate draft of branch 1
+                   [-1, -1, -1, 4, 3, 9]], np.int32)
+    parent = np.array([-1, 0, 0, 0], np.int32)
+    rows = O.masked_rows(st)
+    lg = (rng.standard_normal((rows.size, V)) * 1.28).astype(np.float32)
+    r00, r01, r02 = 0, 1, 2
+    lg[r01] = lg[r00]                  # identical rows -> equal S -> lower position wins
+    lg[r02, 11] = lg[r02].max() + 2.0  # a third, clearly less confident position
+    lg[r00, 7] = lg[r00].max() + 6.0   # token 7, very confident
+    lg[r01, 7] = lg[r01].max() + 6.0
+    lg[r00, 5] = lg[r00, 7]            # token tie at T = 0 -> lowest id (5)
+    lg[r01, 5] = lg[r01, 7]
+    x = dict(state=st, parent=parent)
+    for T in (0.0, 1.0):
+        res = _run_commit_match(st, parent, V, T, 3, 40, 100, lg)
+        check_commit_match(x, res, T, 3, 40, 100, 1, logits_host=lg)
+    res = _run_commit_match(st, parent, V, 0.0, 3, 40, 100, lg)
+    assert res["commit_pos"][0, 0] == 0 and res["token"][0] == 5
+
+
+def test_duplicate_draft_lowest_index(gpu_lib):
+    V, N = 1024, 4
+    st0 = np.array([-1, -1, 2, 3], np.int32)
+    rows0 = O.masked_rows(st0[None])
+    lg0 = synth.state_keyed_logits(11, st0, V)[rows0]
+    nxt, *_ = O.commit(lg0, rows0, st0[None], np.array([-1]), 0.0, 11, 5, 0)
+    decoy = st0.copy(); decoy[0] = (nxt[0][0] + 1) % V if nxt[0][0] != -1 else 1; decoy[1] = -1
+    st = np.stack([st0, decoy, nxt[0], nxt[0], nxt[0]]).astype(np.int32)
+    parent = np.array([-1, 0, 0, 0, 0], np.int32)
+    rows = O.masked_rows(st)
+    lg = np.stack([synth.state_keyed_logits(11, st[r // N], V)[r % N] for r in rows])
+    res = _run_commit_match(st, parent, V, 0.0, 11, 5, 0, lg)
+    x = dict(state=st, parent=parent)
+    check_commit_match(x, res, 0.0, 11, 5, 0, 1, logits_host=lg)
+    assert res["chain"][0] == 2
+
+
+def test_state_violation_status(gpu_lib):
+    V, N = 512, 4
+    st = np.array([[-1, -1, -1, 3], [1, 2, -1, 3], [1, 5, -1, 3]], np.int32)
+    parent = np.array([-1, 0, 0], np.int32)
+    rows = O.masked_rows(st)
+    lg = np.random.default_rng(1).standard_normal((rows.size, V)).astype(np.float32)
+    res = _run_commit_match(st, parent, V, 0.0, 1, 1, 0, lg, S_max=1)
+    assert res["status"] == O.SFV_E_STATE and res["h"] == 0 and np.all(res["chain"] == -1)
+    res = _run_commit_match(st, parent, V, 0.0, 1, 1, 0, lg, S_max=2)
+    assert res["status"] == O.SFV_OK
+
+
+# ---------------------------------------------------------------------------
+# ragged and degenerate shapes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [
+    dict(B1=5, N=7, L=100, Hq=8, Hkv=1, d=64),
+    dict(B1=2, N=1, L=0, Hq=2, Hkv=2, d=32),
+    dict(B1=1, N=64, L=1000, Hq=16, Hkv=2, d=128),
+    dict(B1=64, N=3, L=70, Hq=4, Hkv=4, d=128),
+    dict(B1=3, N=256, L=130, Hq=2, Hkv=1, d=32),
+])
+def test_attention_ragged(gpu_lib, shape):
+    rng = np.random.default_rng(9)
+    B1, N, L, Hq, Hkv, d = (shape[k] for k in ("B1", "N", "L", "Hq", "Hkv", "d"))
+    say(f"attention ragged {shape}")
+    x = dict(q=synth.f32_to_bf16_bits(rng.standard_normal((B1, N, Hq, d), dtype=np.float32)),
+             k_blk=synth.f32_to_bf16_bits(rng.standard_normal((B1, N, Hkv, d), dtype=np.float32)),
+             v_blk=synth.f32_to_bf16_bits(rng.standard_normal((B1, N, Hkv, d), dtype=np.float32)),
+             k_ctx=synth.f32_to_bf16_bits(rng.standard_normal((Hkv, max(L, 1), d), dtype=np.float32))[:, :L],
+             v_ctx=synth.f32_to_bf16_bits(rng.standard_normal((Hkv, max(L, 1), d), dtype=np.float32))[:, :L])
+    xd = to_device(x)
+    step = VerifyStep(B1, N, L, Hq, Hkv, d, 64, 8, 0, [-1] + [0] * (B1 - 1), 0.0, 1, 1, 0)
+    step.attend(xd)
+    torch.cuda.synchronize()
+    check_attention(x, step, full=True)
+
+
+@pytest.mark.parametrize("M,D,V", [(1, 64, 8), (5, 128, 1000), (130, 192, 1001), (257, 4096, 2048)])
+def test_lm_head_ragged(gpu_lib, M, D, V):
+    rng = np.random.default_rng(M)
+    R = M + 3
+    say(f"lm_head ragged M={M} D={D} V={V}")
+    hidden = synth.f32_to_bf16_bits(rng.standard_normal((R, D), dtype=np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((V, D)) * 0.05).astype(np.float32))
+    rows = np.sort(rng.choice(R, M, replace=False)).astype(np.int32)
+    hd = torch.from_numpy(hidden).view(torch.bfloat16).cuda()
+    wd = torch.from_numpy(w).view(torch.bfloat16).cuda()
+    rd = torch.from_numpy(rows).cuda()
+    out = torch.full((M, V), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.sfv_lm_head(hd, rd, M, R, wd, D, V, out)
+    torch.cuda.synchronize()
+    ref = O.lm_head(f32(hidden), rows, f32(w))
+    err = np.max(np.abs(out.cpu().numpy() - ref))
+    assert err <= LOGIT_ABS
+
+
+@pytest.mark.parametrize("fill", ["none", "all", "random"])
+def test_masked_rows_edges(gpu_lib, fill):
+    rng = np.random.default_rng(2)
+    B1, N = 64, 256
+    st = rng.integers(0, 100, (B1, N)).astype(np.int32)
+    if fill == "all":
+        st[:] = -1
+    elif fill == "random":
+        st[rng.random((B1, N)) < 0.3] = -1
+    rows = torch.full((B1 * N,), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gpu_lib.sfv_masked_rows(torch.from_numpy(st).cuda(), B1, N, rows, cnt)
+    torch.cuda.synchronize()
+    ref = O.masked_rows(st)
+    assert int(cnt.item()) == ref.size
+    assert np.array_equal(rows[:ref.size].cpu().numpy(), ref)
+
+
+def test_commit_nothing_masked(gpu_lib):
+    st = np.array([[1, 2, 3], [1, 2, 3]], np.int32)
+    parent = np.array([-1, 0], np.int32)
+    step = VerifyStep(2, 3, 0, 1, 1, 32, 64, 8, 0, parent, 1.0, 1, 1, 0, S_max=0)
+    xd = {"state": torch.from_numpy(st).cuda()}
+    step.masked_rows(xd)
+    step.commit(xd, logits=torch.zeros((1, 8), device="cuda"))
+    step.match(xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(step.next_state.cpu().numpy(), st)
+    assert np.all(step.commit_pos.cpu().numpy() == -1)
+    assert int(step.n_accepted.item()) == 0
