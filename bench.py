@@ -1,0 +1,184 @@
+"""Throughput of one multi-branch verification step on one MI355X.
+
+A step is the whole hot path over one batch: shared-prefix attention of every
+branch, masked-row scan, LM head over the masked rows, commit, and the
+draft-tree match, with all inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+
+value = B1*N branch-tokens verified per step / seconds per step.  The roofline
+object reports the dominant kernel (the LM head) against the HBM peak, timed
+with HIP events on the stream the kernels run on; cpu_baseline times the CPU
+oracle on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified branch-tokens/s per verify step; % HBM peak (attn) and % MFMA peak (LM head)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lm_head_sdar8b_budget8_counters.md")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-only", action="store_true", help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+def algorithmic(wl, M):
+    """Bytes and flops each kernel must move/compute (context K/V read once)."""
+    B1, N, L, Hq, Hkv, d, D, V = wl.B1, wl.N, wl.L, wl.Hq, wl.Hkv, wl.d, wl.D, wl.V
+    R = B1 * N
+    attn_bytes = 2 * (R * Hq * d * 2 + 2 * R * Hkv * d + 2 * Hkv * L * d) + 4 * R * Hq
+    attn_flop = 4 * R * Hq * d * (L + N)
+    lm_bytes = 2 * V * D + 2 * M * D + 4 * M * V + 4 * M
+    lm_flop = 2 * M * D * V
+    commit_bytes = 4 * M * V + 4 * 2 * R + 8 * M
+    return dict(attention=(attn_bytes, attn_flop), lm_head=(lm_bytes, lm_flop),
+                commit=(commit_bytes, 0))
+
+
+def source_digest(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per LM-head launch from the committed counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    text = open(PROFILE_TRAFFIC).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    s = re.search(r"lm_head_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not s:
+        return None
+    here = source_digest(os.path.join(ROOT, "branch_verify_amd", "csrc", "lm_head.hip"))
+    return float(m.group(1)) if s.group(1) == here else None
+
+
+def cpu_baseline(wl, x):
+    """The CPU oracle over the same workload (one full step), on this host."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from branch_verify_amd import synth
+    from oracle import oracle as O
+    f = synth.bf16_bits_to_f32
+    args = [f(x[k]) for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx", "hidden")]
+    w = f(x["w"])
+    times = []
+    while len(times) < 10 and sum(times) < 10.0:   # about 10 s of CPU work
+        t0 = time.perf_counter()
+        O.verify_step(*args, w, x["state"], x["parent"], wl.T, wl.seed, wl.step0, wl.pos0,
+                      1.0 / np.sqrt(wl.d), S_max=wl.S_t)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": wl.B1 * wl.N / dt, "unit": "branch-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(times)} full verify steps of {wl.name} (fp64 numpy oracle), "
+                      f"median {dt:.2f} s per step"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the step is not "
+              "sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from branch_verify_amd import synth
+    from branch_verify_amd.step import step_for, to_device
+
+    wl = synth.WORKLOADS[a.workload]
+    x = synth.draw_inputs(wl)
+    M = synth.masked_count(x["state"])
+    if a.cpu_only:
+        print(json.dumps(cpu_baseline(wl, x)))
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    xd = to_device(x)
+    step = step_for(wl, x)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(a.warmup):
+        step.run(xd)
+    torch.cuda.synchronize()
+
+    names = ["attention", "masked_rows", "lm_head", "commit", "match"]
+    calls = [step.attend, step.masked_rows, step.lm_head, lambda z: step.commit(z), step.match]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in names] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        for j, fn in enumerate(calls):
+            ev[s][j][0].record(stream)
+            fn(xd)
+            ev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per = {n: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(a.steps)])) * 1e3
+           for j, n in enumerate(names)}  # microseconds
+    ms_per_step = elapsed / a.steps * 1e3
+    alg = algorithmic(wl, M)
+    lm_bytes, lm_flop = alg["lm_head"]
+    lm_s = per["lm_head"] * 1e-6
+    achieved = lm_bytes / lm_s / 1e9
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": wl.B1 * wl.N / (elapsed / a.steps),
+        "unit": "branch-tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B1": wl.B1, "N": wl.N, "L": wl.L, "Hq": wl.Hq,
+                   "Hkv": wl.Hkv, "d": wl.d, "D": wl.D, "V": wl.V, "masked_rows": M,
+                   "temperature": wl.T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "lm_head", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "mfma_frac": lm_flop / lm_s / 1e12 / BF16_PEAK_TFLOPS},
+        "kernels_us": per,
+    }
+    ab, af = alg["attention"]
+    out["attention_roofline"] = {"hbm_frac": ab / (per["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                 "mfma_frac": af / (per["attention"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
+    cb, _ = alg["commit"]
+    out["commit_roofline"] = {"hbm_frac": cb / (per["commit"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, x)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
