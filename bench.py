@@ -30,6 +30,10 @@ BF16_PEAK_TFLOPS = 2500.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lm_head_sdar8b_budget8_counters.md")
 
 
+def note(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +114,7 @@ def main():
     from branch_verify_amd.step import step_for, to_device
 
     wl = synth.WORKLOADS[a.workload]
+    note(f"drawing inputs of {wl.name}")
     x = synth.draw_inputs(wl)
     M = synth.masked_count(x["state"])
     if a.cpu_only:
@@ -120,6 +125,7 @@ def main():
     step = step_for(wl, x)
     stream = torch.cuda.current_stream()
 
+    note(f"{a.warmup} warm-up steps, then {a.steps} timed steps")
     for _ in range(a.warmup):
         step.run(xd)
     torch.cuda.synchronize()
@@ -174,6 +180,7 @@ def main():
     cb, _ = alg["commit"]
     out["commit_roofline"] = {"hbm_frac": cb / (per["commit"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
     if not a.no_cpu_baseline:
+        note("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(wl, x)
     else:
         out["cpu_baseline"] = None
