@@ -9,6 +9,9 @@ namespace sfv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+// 16 bytes as a first-class vector (uint4 is a struct: copying it from global
+// memory goes through memcpy and can keep register arrays out of registers).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -44,6 +47,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   __builtin_memcpy(&r, &v, 16);
   return r;
 }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -2,16 +2,36 @@
 // bf16 in, fp32 accumulate and out, on v_mfma_f32_32x32x16_bf16.
 //
 // SpecFold, Appendix B, keeps the LM head as a plain dense library product;
-// here it is the dominant step of a one-layer verify pass (the weight is
-// ~1.2 GB of bf16 and is streamed once per pass).  Design for gfx950:
-//  * The product is computed transposed (vocab x rows) so that each lane ends
-//    with 4 consecutive vocab ids of one row and stores them as one 16-byte
-//    write of the row-major logits.
-//  * Workgroup tile 128 vocab x 128 rows x 64 k, four waves of 64 x 64,
-//    double-buffered LDS with the next k-tile prefetched into registers.
-//  * The row tiles of one vocab tile get consecutive logical ids on one XCD,
-//    so the weight tile they share is read from HBM once and then hit in L2.
-//  * Masked rows are gathered on the fly from hidden through `rows`.
+// here it is the dominant step of a one-layer verify pass: the weight is
+// ~1.2 GB of bf16 and must be streamed from HBM once per pass.  Both kernels
+// compute the product transposed (vocab x rows), so that each lane ends with
+// 4 consecutive vocab ids of one row and stores them as one 16-byte write of
+// the row-major logits, and both gather the masked rows through `rows`.
+//
+// lm_head_tiled (M <= 128, and M > 256): 128 vocab x 128 rows x 64 k tiles,
+// four waves of 64 x 64, double-buffered LDS with the next k-tile prefetched
+// into registers; the row tiles of one vocab tile get consecutive logical ids
+// on one XCD, so the weight tile they share is read from HBM once and then
+// hit in L2.
+//
+// lm_head_stream (129..256 rows, the weight-streaming regime):
+//  * Every row of the padded row set is in one workgroup, so W is read from
+//    HBM exactly once and no MFMA work is spent on more than 31 pad rows.
+//  * Each wave owns 32 vocab rows and loads them from HBM straight into the
+//    MFMA A-operand registers, P k-stages ahead of use: no LDS round trip on
+//    the W path.  The reduction index k is permuted identically on both
+//    operands (slot (half, j) of step s holds k = 32*half + 8*s + j), which
+//    leaves the sum unchanged and makes a lane's 64 bytes per stage contiguous.
+//  * The gathered hidden rows (the operand the four waves share) are staged
+//    per 64-wide k-stage in double-buffered LDS.
+//  * One persistent workgroup per CU walks its tiles over a flattened
+//    (tile, k-stage) index, so prefetch runs across tile boundaries and the
+//    1187 vocab tiles (a prime count for V = 151936) spread within one tile.
+//
+// Every global load is unconditional: pad vocab ids and pad rows read a
+// clamped, in-bounds address and the outputs they pollute are never stored.
+// (A conditional load makes the compiler drain all outstanding loads, the
+// prefetched stages included, before each use.)
 #include "common.h"
 #include "internal.h"
 
@@ -23,6 +43,7 @@ constexpr int BV = 128;  // vocab per tile
 constexpr int BM = 128;  // rows per tile
 constexpr int BK = 64;   // k per stage
 constexpr int LDK = BK + 8;
+constexpr int kStreamRows = 256;  // largest row count served by lm_head_stream
 
 struct Params {
   const unsigned short* hidden;
@@ -33,7 +54,7 @@ struct Params {
   int vt, mt;  // tile counts
 };
 
-__global__ __launch_bounds__(kThreads) void lm_head_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) void lm_head_tiled(Params p) {
   __shared__ unsigned short ws[2][BV][LDK];
   __shared__ unsigned short hs[2][BM][LDK];
 
@@ -53,28 +74,28 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(Params p) {
 
   // Each thread stages 4 chunks of 16 bytes of W and of hidden per k-tile:
   // chunk c = t + 256*i -> tile row c / 8, k part c % 8.
+  // Loads are unconditional (clamped in-bounds addresses for pad vocab ids
+  // and pad rows, whose outputs are never stored), so that the compiler keeps
+  // the prefetch of the next k-tile in flight across the MFMAs.
   const unsigned short* wsrc[4];
   const unsigned short* hsrc[4];
-  bool wok[4], hok[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = t + kThreads * i;
     const int r = c / 8, part = c % 8;
-    const int v = v0 + r;
-    wok[i] = v < p.V;
-    wsrc[i] = p.w + (size_t)(wok[i] ? v : 0) * p.D + part * 8;
-    const int m = m0 + r;
-    hok[i] = m < p.M;
-    const int hr = hok[i] ? min(max(p.rows[m], 0), p.R - 1) : 0;  // never leave hidden
+    const int v = min(v0 + r, p.V - 1);
+    wsrc[i] = p.w + (size_t)v * p.D + part * 8;
+    const int m = min(m0 + r, p.M - 1);
+    const int hr = min(max(p.rows[m], 0), p.R - 1);  // never leave hidden
     hsrc[i] = p.hidden + (size_t)hr * p.D + part * 8;
   }
 
-  uint4 wreg[4], hreg[4];
+  u32x4 wreg[4], hreg[4];
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      wreg[i] = wok[i] ? *(const uint4*)(wsrc[i] + k0) : make_uint4(0, 0, 0, 0);
-      hreg[i] = hok[i] ? *(const uint4*)(hsrc[i] + k0) : make_uint4(0, 0, 0, 0);
+      wreg[i] = ld16(wsrc[i] + k0);
+      hreg[i] = ld16(hsrc[i] + k0);
     }
   };
   auto stash = [&](int buf) {
@@ -82,8 +103,8 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(Params p) {
     for (int i = 0; i < 4; ++i) {
       const int c = t + kThreads * i;
       const int r = c / 8, part = c % 8;
-      *(uint4*)(&ws[buf][r][part * 8]) = wreg[i];
-      *(uint4*)(&hs[buf][r][part * 8]) = hreg[i];
+      st16(&ws[buf][r][part * 8], wreg[i]);
+      st16(&hs[buf][r][part * 8], hreg[i]);
     }
   };
 
@@ -94,21 +115,20 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(Params p) {
     for (int b = 0; b < 2; ++b) acc[a][b] = floatx16{};
 
   const int ksteps = p.D / BK;
+  const int klast = (ksteps - 1) * BK;
   fetch(0);
   stash(0);
   __syncthreads();
   for (int ks = 0; ks < ksteps; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < ksteps) fetch((ks + 1) * BK);
+    fetch(min((ks + 1) * BK, klast));  // past the end: re-reads the last tile (L2 hit)
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      uint4 af[2], bfr[2];
+      u32x4 af[2], bfr[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = *(const uint4*)(&ws[buf][wv * 64 + a * 32 + col][kk * 16 + half * 8]);
+      for (int a = 0; a < 2; ++a) af[a] = ld16(&ws[buf][wv * 64 + a * 32 + col][kk * 16 + half * 8]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bfr[b] = *(const uint4*)(&hs[buf][wm * 64 + b * 32 + col][kk * 16 + half * 8]);
+      for (int b = 0; b < 2; ++b) bfr[b] = ld16(&hs[buf][wm * 64 + b * 32 + col][kk * 16 + half * 8]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -116,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(Params p) {
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[a]), as_bf16x8(bfr[b]),
                                                                acc[a][b], 0, 0, 0);
     }
-    if (ks + 1 < ksteps) stash(buf ^ 1);
+    stash(buf ^ 1);
     __syncthreads();
   }
 
@@ -146,6 +166,193 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(Params p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// persistent weight-streaming kernel: one workgroup per CU
+// ---------------------------------------------------------------------------
+// A workgroup tile is 128*VW vocab ids x all (padded) rows.  The hidden rows
+// are the operand shared by the whole tile and are re-read from L2 once per
+// tile, so wide tiles (VW = 2: 256 ids) halve that traffic.  Each CU runs one
+// workgroup that walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... over a
+// flattened (tile, k-stage) index: W and hidden are prefetched P stages ahead
+// straight across tile boundaries, and the tiles per CU differ by at most one
+// (a CU with deep prefetch can pull well above its fair share of HBM, so the
+// last, partial round still streams at full rate).  The LDS is padded so that
+// no second workgroup fits a CU.
+template <int MB, int VW, int P>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_head_stream(Params p) {
+  constexpr int MP = MB * 32;
+  constexpr int MPA = MP > 288 ? MP : 288;  // LDS rows allocated (>= 81 KB: one workgroup per CU)
+  constexpr int SK = 64;
+  constexpr int LDH = SK + 8;
+  constexpr int TV = 128 * VW;  // vocab ids per tile
+  __shared__ unsigned short hs[2][MPA][LDH];
+
+  const int t = threadIdx.x;
+  const int lane = t % kWave;
+  const int wave = t / kWave;
+  const int r = lane % 32;
+  const int half = lane / 32;
+  const int ksteps = p.D / SK;
+  const int ntiles = (p.V + TV - 1) / TV;
+  const int my_tiles = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int total = my_tiles * ksteps;  // a multiple of P (the launcher checks ksteps % P)
+
+  // hidden chunk c = t + 256*i -> padded row c / 8, k part c % 8 (same for every tile)
+  const unsigned short* hsrc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int c = t + kThreads * i;
+    const int m = min(c / (SK / 8), p.M - 1);
+    const int hr = min(max(p.rows[m], 0), p.R - 1);  // never leave hidden
+    hsrc[i] = p.hidden + (size_t)hr * p.D + (c % (SK / 8)) * 8;
+  }
+  const unsigned short* wlane = p.w + 32 * half;
+
+  // this lane's W rows of a tile: tile*TV + wave*32*VW + 32*b + r.  W comes
+  // from HBM and is prefetched P stages ahead; hidden comes from L2 and is
+  // loaded one stage ahead (registers are the limit on prefetch depth).
+  u32x4 wreg[P][VW][4];
+  u32x4 hreg[MB];
+  // Flattened stage g (clamped to the last one: a re-read, an L2 hit).
+  auto stage_tile = [&](int g) { return (int)blockIdx.x + (min(g, total - 1) / ksteps) * (int)gridDim.x; };
+  auto stage_k = [&](int g) { return (min(g, total - 1) % ksteps) * SK; };
+  auto load_w = [&](u32x4 (&wd)[VW][4], int g) {
+    const int tile = stage_tile(g);
+    const int k0 = stage_k(g);
+#pragma unroll
+    for (int b = 0; b < VW; ++b) {
+      const int v = min(tile * TV + wave * 32 * VW + 32 * b + r, p.V - 1);
+      const unsigned short* src = wlane + (size_t)v * p.D + k0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wd[b][s] = ld16(src + 8 * s);
+    }
+  };
+  auto load_h = [&](int g) {
+    const int k0 = stage_k(g);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) hreg[i] = ld16(hsrc[i] + k0);
+  };
+  auto store_h = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int c = t + kThreads * i;
+      st16(&hs[buf][c / (SK / 8)][(c % (SK / 8)) * 8], hreg[i]);
+    }
+  };
+
+  floatx16 acc[VW][MB];
+#pragma unroll
+  for (int b = 0; b < VW; ++b)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[b][mb] = floatx16{};
+
+  if (total > 0) {
+    load_h(0);
+#pragma unroll
+    for (int j = 0; j < P; ++j) load_w(wreg[j], j);
+    store_h(0);
+    __syncthreads();
+  }
+  for (int g0 = 0; g0 < total; g0 += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int g = g0 + j;
+      const int buf = g & 1;
+      load_h(g + 1);
+      // Every hidden fragment of the stage is read before the first MFMA (the
+      // scheduling barrier keeps them together), so the stage pays one LDS
+      // latency instead of one per fragment.
+      u32x4 hf[4][MB];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) hf[s][mb] = ld16(&hs[buf][mb * 32 + r][32 * half + 8 * s]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int b = 0; b < VW; ++b)
+            acc[b][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wreg[j][b][s]), as_bf16x8(hf[s][mb]),
+                                                                 acc[b][mb], 0, 0, 0);
+        }
+      }
+      load_w(wreg[j], g + P);
+      store_h(buf ^ 1);
+      if (g % ksteps == ksteps - 1) {  // last stage of a tile: write it out
+        const int tile = (int)blockIdx.x + (g / ksteps) * (int)gridDim.x;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int m = mb * 32 + r;
+          if (m < p.M) {
+            float* out = p.logits + (size_t)m * p.V;
+#pragma unroll
+            for (int b = 0; b < VW; ++b) {
+              const int vb = tile * TV + wave * 32 * VW + 32 * b;
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const int v = vb + 8 * q4 + 4 * half;
+                const float4 val = make_float4(acc[b][mb][4 * q4], acc[b][mb][4 * q4 + 1],
+                                               acc[b][mb][4 * q4 + 2], acc[b][mb][4 * q4 + 3]);
+                if (v + 3 < p.V && (p.V % 4) == 0) {
+                  *(float4*)(out + v) = val;
+                } else {
+                  if (v + 0 < p.V) out[v + 0] = val.x;
+                  if (v + 1 < p.V) out[v + 1] = val.y;
+                  if (v + 2 < p.V) out[v + 2] = val.z;
+                  if (v + 3 < p.V) out[v + 3] = val.w;
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < VW; ++b) acc[b][mb] = floatx16{};
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int MB, int VW, int P>
+hipError_t launch_stream(const Params& p, hipStream_t stream) {
+  if ((p.D / 64) % P != 0) return hipErrorInvalidValue;
+  const int ntiles = (p.V + 128 * VW - 1) / (128 * VW);
+  const int grid = min(ntiles, cu_count());
+  hipLaunchKernelGGL((lm_head_stream<MB, VW, P>), dim3(grid), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_stream_m(const Params& p, hipStream_t stream) {
+  switch ((p.M + 31) / 32) {
+    case 5: return launch_stream<5, 1, P>(p, stream);
+    case 6: return launch_stream<6, 1, P>(p, stream);
+    case 7: return launch_stream<7, 1, (P > 2 ? 2 : P)>(p, stream);
+    case 8: return launch_stream<8, 1, (P > 2 ? 2 : P)>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_tiled(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL(lm_head_tiled, dim3(p.vt * p.mt), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R, const void* w,
@@ -162,8 +369,16 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   p.R = R;
   p.vt = (V + BV - 1) / BV;
   p.mt = (M + BM - 1) / BM;
-  hipLaunchKernelGGL(lm_head_kernel, dim3(p.vt * p.mt), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  // One 128-row tile: the tiled kernel.  129..256 rows: stream the weight
+  // once past every row (the tiled kernel would run two row tiles).
+  if (M <= BM || M > kStreamRows) return launch_tiled(p, stream);
+  // Prefetch depth: 4 stages while the registers allow it (up to 192 rows),
+  // else 2; it must divide the number of 64-wide k-stages.
+  const int ks = D / 64;
+  const int want = M <= 192 ? 4 : 2;
+  if (want == 4 && ks % 4 == 0) return launch_stream_m<4>(p, stream);
+  if (ks % 2 == 0) return launch_stream_m<2>(p, stream);
+  return launch_stream_m<1>(p, stream);
 }
 
 }  // namespace sfv
