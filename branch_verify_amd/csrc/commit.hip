@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
 
   const int item = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
-  if (item >= *ws.count) return;
+  if (NOISY && item >= *ws.count) return;  // at T = 0 there is one item per row, M in all
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
 
   int nrows, row[R];
@@ -307,11 +307,33 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
     kidx[k] = 0x7FFFFFFF;
   }
 
+  // Logit loads are unconditional: a lane past the range end reads the last
+  // 8 ids of the range and then replaces the values by -inf, so the compiler
+  // never has to drain outstanding loads at a branch.  At T = 0 the next
+  // iteration's logits are loaded before this one's are used.
+  const float* rbase[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) rbase[k] = a.logits + (size_t)(k < nrows ? row[k] : row[0]) * a.V;
+  const int vlast = ve - 8;  // ve - vb >= 8: both are multiples of 8
+  float4 pf0 = make_float4(0.f, 0.f, 0.f, 0.f), pf1 = pf0;
+  if (!NOISY) {
+    const int vc = min(vb + 8 * t, vlast);
+    pf0 = *(const float4*)(rbase[0] + vc);
+    pf1 = *(const float4*)(rbase[0] + vc + 4);
+  }
+
   // The trip count is uniform across the workgroup (cross-lane reductions run
   // inside the loop); a lane past the range end keeps every value at -inf.
   for (int v0 = vb; v0 < ve; v0 += kPerIter) {
     const int v = v0 + 8 * t;
     const bool active = v < ve;  // ve and v are multiples of 8
+    const int vc = min(v, vlast);
+    float4 nf0 = pf0, nf1 = pf1;
+    if (!NOISY) {
+      const int vn = min(v + kPerIter, vlast);
+      nf0 = *(const float4*)(rbase[0] + vn);
+      nf1 = *(const float4*)(rbase[0] + vn + 4);
+    }
     unsigned wd[8];
     float gf[8];
     if (NOISY) {
@@ -319,41 +341,48 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
 #pragma unroll
       for (int e = 0; e < 8; ++e) gf[e] = gumbel_fast(wd[e]);
     }
+    // (predicated blocks, not breaks, so that every loop unrolls and the small
+    // arrays stay in registers)
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-      if (k >= nrows) break;
-      float4 x0 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY), x1 = x0;
-      if (active) {
-        const float* src = a.logits + (size_t)row[k] * a.V + v;
-        x0 = *(const float4*)src;
-        x1 = *(const float4*)(src + 4);
+      if (k < nrows) {
+      float4 x0, x1;
+      if (!NOISY) {
+        x0 = pf0;
+        x1 = pf1;
+      } else {
+        x0 = *(const float4*)(rbase[k] + vc);
+        x1 = *(const float4*)(rbase[k] + vc + 4);
       }
+      // (an inactive lane's values are never used: the sums below are guarded
+      // and its Gumbel keys are -inf)
       const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       // running max / first argmax and the confidence sum (this lane's ids)
+      if (active) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (!active) break;
-        const float xe = x[e];
-        if (xe > lmax[k]) {
-          if (lmax[k] != -INFINITY) {
-            const float af = xe - lmax[k];
-            const float f = fast_exp2(-af * kLog2e);
-            S[k] *= (double)f;
-            E[k] = E[k] * f + (float)S[k] * (kC1 * af + kC2);
+        for (int e = 0; e < 8; ++e) {
+          const float xe = x[e];
+          if (xe > lmax[k]) {
+            if (lmax[k] != -INFINITY) {
+              const float af = xe - lmax[k];
+              const float f = fast_exp2(-af * kLog2e);
+              S[k] *= (double)f;
+              E[k] = E[k] * f + (float)S[k] * (kC1 * af + kC2);
+            }
+            lmax[k] = xe;
+            lidx[k] = v + e;
           }
-          lmax[k] = xe;
-          lidx[k] = v + e;
+          const float am = lmax[k] - xe;
+          const float tt = fast_exp2(-am * kLog2e);
+          S[k] += (double)tt;
+          E[k] += tt * (kC1 * am + kC2);
         }
-        const float am = lmax[k] - xe;
-        const float tt = fast_exp2(-am * kLog2e);
-        S[k] += (double)tt;
-        E[k] += tt * (kC1 * am + kC2);
       }
       if (NOISY) {
         float ka[8], lm = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          ka[e] = (x[e] * a.inv_t) + gf[e];
+          ka[e] = active ? (x[e] * a.inv_t) + gf[e] : -INFINITY;
           lm = fmaxf(lm, ka[e]);
         }
         wbest[k] = fmaxf(wbest[k], wave_max(lm));
@@ -369,7 +398,10 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
           }
         }
       }
+      }
     }
+    pf0 = nf0;
+    pf1 = nf1;
   }
 
   // ---- reduce over the workgroup, row by row ----
@@ -475,16 +507,19 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
 // ---------------------------------------------------------------------------
 struct FinArgs {
   const float* logits;
+  const int32_t* rows;
   const int32_t* state;
   int32_t* next_state;
   int32_t* commit_pos;
   int32_t* token;
   float* conf;
-  int N, V, splits;
+  int M, N, V, splits;
   bool noisy;
 };
 
+// One workgroup per branch.
 __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, WsLayout ws) {
+  __shared__ int lmap[kMaxBlock];  // position -> masked row, -1 if none
   __shared__ double sS[kMaxBlock];
   __shared__ float sE[kMaxBlock];
   __shared__ float sM[kMaxBlock];
@@ -492,17 +527,24 @@ __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, Ws
   __shared__ int sCand[kMaxBlock];
   __shared__ double red[kThreads / kWave];
   __shared__ int best_n_s, ncand_s;
-  __shared__ double lo_s, hi_s;
 
   const int i = blockIdx.x;
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int N = a.N;
+  const int f0 = i * N;
+  for (int n = t; n < N; n += kThreads) lmap[n] = -1;
+  __syncthreads();
+  for (int r = t; r < a.M; r += kThreads) {  // the rows of this branch's positions
+    const int f = a.rows[r];
+    if (f >= f0 && f < f0 + N) lmap[f - f0] = r;
+  }
+  __syncthreads();
+
+  // merge the vocab ranges of each masked position: token, S and its error bound
   for (int n = t; n < N; n += kThreads) {
-    const int f = i * N + n;
     sS[n] = -1.0;  // not masked
-    if (a.state[f] != -1) continue;
-    const int r = ws.rowmap[f];
-    if (r < 0) continue;
+    const int r = lmap[n];
+    if (a.state[f0 + n] != -1 || r < 0) continue;
     const Partial* pp = ws.part + (size_t)r * a.splits;
     float M = -INFINITY, km = -INFINITY;
     int mi = 0x7FFFFFFF, ki = 0x7FFFFFFF;
@@ -533,23 +575,41 @@ __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, Ws
     sTok[n] = tok;
   }
   __syncthreads();
-  if (t == 0) {
+
+  // Smallest S (highest confidence), ties to the lowest position, then every
+  // position whose interval [S - E, S + E] reaches the best one's upper end.
+  if (wave == 0) {
+    double bs = 0.0;
     int bn = -1;
-    for (int n = 0; n < N; ++n) {
-      if (sS[n] < 0.0) continue;
-      if (bn < 0 || sS[n] < sS[bn]) bn = n;
-    }
-    best_n_s = bn;
-    if (bn >= 0) {
-      hi_s = sS[bn] + (double)sE[bn];
-      int c = 0;
-      for (int n = 0; n < N; ++n) {
-        if (sS[n] < 0.0) continue;
-        if (sS[n] - (double)sE[n] <= hi_s) sCand[c++] = n;
+    for (int n = lane; n < N; n += kWave) {
+      if (sS[n] >= 0.0 && (bn < 0 || sS[n] < bs)) {
+        bs = sS[n];
+        bn = n;
       }
-      ncand_s = c;
-    } else {
-      ncand_s = 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double os = __shfl_xor(bs, o, kWave);
+      const int on = __shfl_xor(bn, o, kWave);
+      if (on >= 0 && (bn < 0 || os < bs || (os == bs && on < bn))) {
+        bs = os;
+        bn = on;
+      }
+    }
+    int cnt = 0;
+    if (bn >= 0) {
+      const double hi = bs + (double)sE[bn];
+      for (int base = 0; base < N; base += kWave) {
+        const int n = base + lane;
+        const bool c = n < N && sS[n] >= 0.0 && sS[n] - (double)sE[n] <= hi;
+        const unsigned long long bal = __ballot(c);
+        if (c) sCand[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = n;
+        cnt += __popcll(bal);
+      }
+    }
+    if (lane == 0) {
+      best_n_s = bn;
+      ncand_s = cnt;
     }
   }
   __syncthreads();
@@ -560,8 +620,7 @@ __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, Ws
     best = -1;
     for (int c = 0; c < ncand_s; ++c) {
       const int n = sCand[c];
-      const int r = ws.rowmap[i * N + n];
-      const float* src = a.logits + (size_t)r * a.V;
+      const float* src = a.logits + (size_t)lmap[n] * a.V;
       const double M = (double)sM[n];
       double s = 0.0;
       for (int v = t; v < a.V; v += kThreads) s += exp((double)src[v] - M);
@@ -579,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, Ws
     }
   }
   for (int n = t; n < N; n += kThreads) {
-    const int f = i * N + n;
+    const int f = f0 + n;
     a.next_state[f] = (n == best) ? sTok[n] : a.state[f];
   }
   if (t == 0) a.commit_pos[i] = best;
@@ -658,9 +717,12 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
                          hipStream_t stream) {
   const bool noisy = temperature > 0.f;
   WsLayout ws = ws_layout(ws_base, tree.B1, N, M, plan.items_max);
-  hipLaunchKernelGGL(commit_plan_kernel, dim3(1), dim3(kThreads), 0, stream, rows, M, N, tree, noisy, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (noisy) {  // work items group the rows of equal (depth, position); at T = 0 an item is a row
+    hipLaunchKernelGGL(commit_plan_kernel, dim3(1), dim3(kThreads), 0, stream, rows, M, N, tree, noisy, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (M > 0) {
     RowsArgs ra;
     ra.logits = logits;
@@ -684,6 +746,8 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
   }
   FinArgs fa;
   fa.logits = logits;
+  fa.rows = rows;
+  fa.M = M;
   fa.state = state;
   fa.next_state = next_state;
   fa.commit_pos = commit_pos;

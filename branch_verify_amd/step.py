@@ -57,6 +57,7 @@ class VerifyStep:
         self.chain = torch.empty(B1, dtype=torch.int32, device=dev)
         self.n_accepted = torch.empty(1, dtype=torch.int32, device=dev)
         self.status = torch.empty(1, dtype=torch.int32, device=dev)
+        self._side = None  # second stream for the attention (created on first overlapped run)
 
     # the individual rows of the hot path -----------------------------------
     def attend(self, x, stream=None):
@@ -81,13 +82,34 @@ class VerifyStep:
         sfv.sfv_match_tree(x["state"], self.next_state, self.commit_pos, self.parent, self.B1,
                            self.N, 1, self.S_max, self.chain, self.n_accepted, self.status, stream)
 
-    def run(self, x, stream=None):
-        """The whole hot path, stream-ordered, no host synchronisation."""
-        self.attend(x, stream)
-        self.masked_rows(x, stream)
-        self.lm_head(x, stream)
-        self.commit(x, stream=stream)
-        self.match(x, stream)
+    def run(self, x, stream=None, overlap=True):
+        """The whole hot path, stream-ordered, no host synchronisation.
+
+        Attention depends only on q/k/v, so with overlap=True it is issued on a
+        second stream after the LM head (which depends on the masked rows only)
+        and joined before the call returns; everything else stays in order on
+        `stream`."""
+        if not overlap:
+            self.attend(x, stream)
+            self.masked_rows(x, stream)
+            self.lm_head(x, stream)
+            self.commit(x, stream=stream)
+            self.match(x, stream)
+            return
+        main = torch.cuda.current_stream() if stream is None else stream
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=main.device)
+            self._fork = torch.cuda.Event()
+            self._join = torch.cuda.Event()
+        self._fork.record(main)
+        self._side.wait_event(self._fork)
+        self.masked_rows(x, main)
+        self.lm_head(x, main)
+        self.attend(x, self._side)
+        self.commit(x, stream=main)
+        self.match(x, main)
+        self._join.record(self._side)
+        main.wait_event(self._join)
 
     def results(self) -> dict:
         torch.cuda.synchronize()

@@ -128,11 +128,13 @@ def check_commit_match(x, res, wl_T, seed, step0, pos0, S_max, logits_host=None)
 
 
 def run_twice(step, xd):
+    """The step overlapped (attention on a second stream), then in order on one
+    stream: every output must be bit-identical."""
     step.run(xd)
     first = step.results()
     snap = {k: (v.clone() if torch.is_tensor(v) else np.copy(v) if isinstance(v, np.ndarray) else v)
             for k, v in first.items()}
-    step.run(xd)
+    step.run(xd, overlap=False)
     second = step.results()
     for k in snap:
         a, b = snap[k], second[k]
