@@ -30,6 +30,13 @@ constexpr int kRows = 128;     // query rows per workgroup, 32 per wave
 constexpr int kKeys = 64;      // keys per LDS tile
 constexpr int kPad = 8;        // bf16 elements of row padding in LDS
 
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Hardware exp2 (v_exp_f32).  Results below 2^-126 may flush to zero; such
+// terms are below 2^-126 of the row's largest term.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 struct Params {
   const unsigned short* q;
   const unsigned short* k_blk;
@@ -41,64 +48,104 @@ struct Params {
   float* ws;  // split partials: O [splits][Hkv][rows][d], m, l [splits][Hkv][rows]
   int B1, N, L, Hq, Hkv, G;
   int rows_total, row_tiles, splits, chunk;
-  float scale_log2;  // softmax scale * log2(e): scores kept in the log2 domain
+  float scale_log2;  // softmax scale * log2(e), applied inside the exp2
 };
 
 template <int D>
 struct Smem {
-  unsigned short k[kKeys][D + kPad];   // key tile, row-major
-  unsigned short vt[D][kKeys + kPad];  // value tile, transposed
+  unsigned short k[2][kKeys][D + kPad];   // key tiles, row-major (double buffered)
+  unsigned short vt[2][D][kKeys + kPad];  // value tiles, transposed
 };
 
-// Stage keys [key0, key0 + count) of one phase into LDS.  In the context phase
-// key k lives at k_ctx[(g*L + k)*D]; in the block phase flat block key k
-// (branch i_lo + k / N) lives at k_blk[((i_lo*N + k)*Hkv + g)*D].
+// Which keys tile j of this workgroup covers: the context tiles of its split,
+// then (last split only) the block keys of the branches in its row tile.
+struct TileRange {
+  bool ctx;
+  int key0, count;
+};
+
+__device__ __forceinline__ TileRange tile_range(const Params& p, int j, int split, int ctx_tiles,
+                                                int blk_keys) {
+  TileRange tr;
+  if (j < ctx_tiles) {
+    tr.ctx = true;
+    tr.key0 = split * p.chunk + j * kKeys;
+    tr.count = min(kKeys, min(p.L, (split + 1) * p.chunk) - tr.key0);
+  } else {
+    tr.ctx = false;
+    tr.key0 = (j - ctx_tiles) * kKeys;
+    tr.count = min(kKeys, blk_keys - tr.key0);
+  }
+  return tr;
+}
+
+// Registers holding one K/V tile between its global loads and its LDS stores.
+// K: chunk c = t + 256*i (i < D/32) is key c / (D/8), dims (c % (D/8)) * 8.
+// V: thread t < 2*D takes keys 4*(t%16) .. +4 and dims 8*(t/16) .. +8, so that
+// its transposed stores (4 keys of one dim, 8 bytes) from 16 consecutive
+// lanes fill one 128-byte LDS row segment.
 template <int D>
-__device__ __forceinline__ void load_tile(Smem<D>& sm, const Params& p, bool ctx, int g, int i_lo,
-                                          int key0, int count) {
+struct TileRegs {
+  u32x4 k[D / 32];
+  u32x4 v[4];
+};
+
+// Loads are unconditional: rows past `count` re-read the tile's last key
+// (their scores are masked to -inf and their probabilities are 0).
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D>& tr, const Params& p, const TileRange& r, int g,
+                                          int i_lo) {
   const int t = threadIdx.x;
-  constexpr int parts = D / 8;  // 16-byte chunks per key row
+  constexpr int parts = D / 8;
   const unsigned short* kbase;
   const unsigned short* vbase;
   size_t stride;
-  if (ctx) {
-    kbase = p.k_ctx + ((size_t)g * p.L + key0) * D;
-    vbase = p.v_ctx + ((size_t)g * p.L + key0) * D;
+  if (r.ctx) {
+    kbase = p.k_ctx + ((size_t)g * p.L + r.key0) * D;
+    vbase = p.v_ctx + ((size_t)g * p.L + r.key0) * D;
     stride = D;
   } else {
-    kbase = p.k_blk + (((size_t)i_lo * p.N + key0) * p.Hkv + g) * D;
-    vbase = p.v_blk + (((size_t)i_lo * p.N + key0) * p.Hkv + g) * D;
+    kbase = p.k_blk + (((size_t)i_lo * p.N + r.key0) * p.Hkv + g) * D;
+    vbase = p.v_blk + (((size_t)i_lo * p.N + r.key0) * p.Hkv + g) * D;
     stride = (size_t)p.Hkv * D;
   }
-  // keys: 64 rows x parts chunks
+  const int last = r.count - 1;
 #pragma unroll
-  for (int c = t; c < kKeys * parts; c += kThreads) {
-    const int key = c / parts, part = c % parts;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < count) val = *(const uint4*)(kbase + key * stride + part * 8);
-    *(uint4*)(&sm.k[key][part * 8]) = val;
+  for (int i = 0; i < D / 32; ++i) {
+    const int c = t + kThreads * i;
+    const int key = min(c / parts, last);
+    tr.k[i] = ld16(kbase + key * stride + (c % parts) * 8);
   }
-  // values: items of 4 keys x 8 dims, written transposed as 4-key runs
+  if (t < 2 * D) {
+    const int kg = t % 16, dg = t / 16;
 #pragma unroll
-  for (int it = t; it < (kKeys / 4) * parts; it += kThreads) {
-    const int dg = it % parts, kg = it / parts;
-    uint4 rows4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kg * 4 + r;
-      rows4[r] = make_uint4(0, 0, 0, 0);
-      if (key < count) rows4[r] = *(const uint4*)(vbase + key * stride + dg * 8);
+    for (int q = 0; q < 4; ++q) {
+      const int key = min(kg * 4 + q, last);
+      tr.v[q] = ld16(vbase + key * stride + dg * 8);
     }
-    const unsigned short* e0 = (const unsigned short*)&rows4[0];
-    const unsigned short* e1 = (const unsigned short*)&rows4[1];
-    const unsigned short* e2 = (const unsigned short*)&rows4[2];
-    const unsigned short* e3 = (const unsigned short*)&rows4[3];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store(Smem<D>& sm, int buf, const TileRegs<D>& tr) {
+  const int t = threadIdx.x;
+  constexpr int parts = D / 8;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int c = t + kThreads * i;
+    st16(&sm.k[buf][c / parts][(c % parts) * 8], tr.k[i]);
+  }
+  if (t < 2 * D) {
+    const int kg = t % 16, dg = t / 16;
+    // 4 keys x 8 dims -> for each dim e, the 4 keys as two bf16 pairs
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint2 w;
-      w.x = (unsigned)e0[e] | ((unsigned)e1[e] << 16);
-      w.y = (unsigned)e2[e] | ((unsigned)e3[e] << 16);
-      *(uint2*)(&sm.vt[dg * 8 + e][kg * 4]) = w;
+      const int w = e / 2;
+      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of two words
+      uint2 out;
+      out.x = __builtin_amdgcn_perm(tr.v[1][w], tr.v[0][w], sel);
+      out.y = __builtin_amdgcn_perm(tr.v[3][w], tr.v[2][w], sel);
+      *(uint2*)(&sm.vt[buf][dg * 8 + e][kg * 4]) = out;
     }
   }
 }
@@ -128,121 +175,132 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int my_branch = row_ok ? rho / NG : -1;
 
   // Q fragment of this lane's row: dims s*16 + half*8 .. +8 for each step s
-  uint4 qf[DS];
+  u32x4 qf[DS];
   {
-    size_t qoff = 0;
-    if (row_ok) {
-      const int bn = rho / p.G, j = rho % p.G;
-      qoff = ((size_t)bn * p.Hq + (size_t)g * p.G + j) * D;
-    }
+    const int rq = min(rho, p.rows_total - 1);
+    const int bn = rq / p.G, j = rq % p.G;
+    const size_t qoff = ((size_t)bn * p.Hq + (size_t)g * p.G + j) * D;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      qf[s] = row_ok ? *(const uint4*)(p.q + qoff + s * 16 + half * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int s = 0; s < DS; ++s) qf[s] = ld16(p.q + qoff + s * 16 + half * 8);
   }
 
   floatx16 acc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) acc[b] = floatx16{};
-  float m_run = -INFINITY;  // running max (log2 domain)
-  float l_run = 0.f;        // running denominator, this half's keys only
+  float m_run = -INFINITY;  // running max of the raw scores q.k
+  float l_run = 0.f;        // running denominator (scaled to m_run), this half's keys only
 
   const int last_row = min(row0 + kRows, p.rows_total) - 1;
   const int i_lo = row0 / NG;
   const int i_hi = last_row / NG;
+  const int ctx_lo = split * p.chunk;
+  const int ctx_keys = max(0, min(p.L, ctx_lo + p.chunk) - ctx_lo);
+  const int ctx_tiles = (ctx_keys + kKeys - 1) / kKeys;
+  const int blk_keys = split == p.splits - 1 ? (i_hi - i_lo + 1) * p.N : 0;
+  const int ntiles = ctx_tiles + (blk_keys + kKeys - 1) / kKeys;
 
-  // phase 0: context keys of this split; phase 1: block keys (last split only)
-  for (int phase = 0; phase < 2; ++phase) {
-    int key_begin, key_end;
-    if (phase == 0) {
-      key_begin = split * p.chunk;
-      key_end = min(p.L, key_begin + p.chunk);
-    } else {
-      if (split != p.splits - 1) break;
-      key_begin = 0;
-      key_end = (i_hi - i_lo + 1) * p.N;
-    }
-    for (int k0 = key_begin; k0 < key_end; k0 += kKeys) {
-      const int count = min(kKeys, key_end - k0);
-      __syncthreads();
-      load_tile<D>(sm, p, phase == 0, g, i_lo, k0, count);
-      __syncthreads();
+  TileRegs<D> tr;
+  if (ntiles > 0) {
+    tile_load<D>(tr, p, tile_range(p, 0, split, ctx_tiles, blk_keys), g, i_lo);
+    tile_store<D>(sm, 0, tr);
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    const TileRange cur = tile_range(p, j, split, ctx_tiles, blk_keys);
+    const bool more = j + 1 < ntiles;
+    if (more) tile_load<D>(tr, p, tile_range(p, j + 1, split, ctx_tiles, blk_keys), g, i_lo);
 
-      // S^T tile: 2 blocks of 32 keys x 32 rows
-      floatx16 st[2];
+    // S^T tile: 2 blocks of 32 keys x 32 rows
+    floatx16 st[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = floatx16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = floatx16{};
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          const uint4 kf = *(const uint4*)(&sm.k[kb * 32 + col][s * 16 + half * 8]);
-          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[s]), st[kb], 0, 0, 0);
-        }
+      for (int s = 0; s < DS; ++s) {
+        const u32x4 kf = ld16(&sm.k[buf][kb * 32 + col][s * 16 + half * 8]);
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[s]), st[kb], 0, 0, 0);
       }
-      // scale, mask, tile max (register r holds key kb*32 + 8*(r/4) + 4*half + r%4)
-      float tmax = -INFINITY;
+    }
+    // Mask (partial context tiles and block tiles only) and tile max of the
+    // raw scores; register r holds key kb*32 + 8*(r/4) + 4*half + r%4.
+    float tmax = -INFINITY;
+    if (cur.ctx && cur.count == kKeys) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kb][r]);
+    } else {
+      // visible keys: kk < count and, in the block phase, kk in this row's branch
+      int lo = 0, hi = cur.count;
+      if (!cur.ctx) {
+        lo = max(lo, (my_branch - i_lo) * p.N - cur.key0);
+        hi = min(hi, (my_branch - i_lo + 1) * p.N - cur.key0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = kb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-          bool vis = kk < count;
-          if (phase == 1) vis = vis && (i_lo + (k0 + kk) / p.N == my_branch);
-          const float sv = vis ? st[kb][r] * p.scale_log2 : -INFINITY;
+          const float sv = (kk >= lo && kk < hi) ? st[kb][r] : -INFINITY;
           st[kb][r] = sv;
           tmax = fmaxf(tmax, sv);
         }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha, m_use;
-      if (m_new == -INFINITY) {  // nothing visible yet for this row
-        alpha = 1.f;
-        m_use = 0.f;
-      } else {
-        alpha = exp2f(m_run - m_new);
-        m_use = m_new;
-      }
-      m_run = m_new;
-      float psum = 0.f;
-      unsigned pk[2][2][4];  // [kb][t2][pair] packed bf16 P
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m_run, tmax);
+    // O and l are rescaled only when some lane's running max moved (elsewhere
+    // the factor is exactly 1).
+    if (__any(m_new > m_run)) {
+      const float alpha = m_new > m_run ? exp2_fast((m_run - m_new) * p.scale_log2) : 1.f;
+      l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2f(st[kb][r] - m_use);
-          const float p1 = exp2f(st[kb][r + 1] - m_use);
-          psum += p0 + p1;
-          pk[kb][r / 8][(r % 8) / 2] = pack_bf16x2(p0, p1);
-        }
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+    }
+    m_run = m_new;
+    const float mc = m_new == -INFINITY ? 0.f : m_new * p.scale_log2;
+    float psum = 0.f;
+    unsigned pk[2][2][4];  // [kb][t2][pair] packed bf16 P
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        floatx2 pp;
+        pp[0] = exp2_fast(fmaf(st[kb][r], p.scale_log2, -mc));
+        pp[1] = exp2_fast(fmaf(st[kb][r + 1], p.scale_log2, -mc));
+        psum += pp[0] + pp[1];
+        pk[kb][r / 8][(r % 8) / 2] = __builtin_bit_cast(unsigned, __builtin_convertvector(pp, bf16x2));
       }
-      // O^T += V^T P^T : A = V^T rows (dims), B = P^T (keys x rows)
+    }
+    l_run += psum;
+    // O^T += V^T P^T : A = V^T rows (dims), B = P^T (keys x rows)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          uint4 pb;
-          pb.x = pk[kb][t2][0];
-          pb.y = pk[kb][t2][1];
-          pb.z = pk[kb][t2][2];
-          pb.w = pk[kb][t2][3];
-          const int kbase = kb * 32 + 16 * t2 + 4 * half;
+      for (int t2 = 0; t2 < 2; ++t2) {
+        u32x4 pb;
+        pb[0] = pk[kb][t2][0];
+        pb[1] = pk[kb][t2][1];
+        pb[2] = pk[kb][t2][2];
+        pb[3] = pk[kb][t2][3];
+        const int kbase = kb * 32 + 16 * t2 + 4 * half;
 #pragma unroll
-          for (int b = 0; b < DB; ++b) {
-            const uint2 lo = *(const uint2*)(&sm.vt[b * 32 + col][kbase]);
-            const uint2 hi = *(const uint2*)(&sm.vt[b * 32 + col][kbase + 8]);
-            const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb), acc[b], 0, 0, 0);
-          }
+        for (int b = 0; b < DB; ++b) {
+          const uint2 lo = *(const uint2*)(&sm.vt[buf][b * 32 + col][kbase]);
+          const uint2 hi = *(const uint2*)(&sm.vt[buf][b * 32 + col][kbase + 8]);
+          u32x4 vf;
+          vf[0] = lo.x;
+          vf[1] = lo.y;
+          vf[2] = hi.x;
+          vf[3] = hi.y;
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb), acc[b], 0, 0, 0);
         }
       }
     }
+    if (more) tile_store<D>(sm, buf ^ 1, tr);
+    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
@@ -263,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
         *(uint2*)(out + dcol) = w;
       }
     }
-    if (half == 0) p.lse[orow] = m_run * 0.69314718055994531f + logf(l_tot);
+    if (half == 0) p.lse[orow] = m_run * p.scale_log2 * 0.69314718055994531f + logf(l_tot);
   } else {
     const size_t prow = ((size_t)split * p.Hkv + g) * p.rows_total + rho;
     float* op = p.ws + prow * D;
@@ -279,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     if (half == 0) {
       const size_t nstate = (size_t)p.splits * p.Hkv * p.rows_total;
       float* mp = p.ws + nstate * D;
-      mp[prow] = m_run;
+      mp[prow] = m_run * p.scale_log2;  // log2 domain (m_run is finite: every split sees a key)
       mp[nstate + prow] = l_tot;
     }
   }
