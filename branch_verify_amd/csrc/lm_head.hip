@@ -8,11 +8,12 @@
 // 4 consecutive vocab ids of one row and stores them as one 16-byte write of
 // the row-major logits, and both gather the masked rows through `rows`.
 //
-// lm_head_tiled (M <= 128, and M > 256): 128 vocab x 128 rows x 64 k tiles,
-// four waves of 64 x 64, double-buffered LDS with the next k-tile prefetched
-// into registers; the row tiles of one vocab tile get consecutive logical ids
-// on one XCD, so the weight tile they share is read from HBM once and then
-// hit in L2.
+// lm_head_tiled (M <= 128): 128 vocab x 128 rows x 64 k tiles, four waves of
+// 64 x 64, double-buffered LDS with the next k-tile prefetched into registers.
+//
+// lm_head_big8 (M > 256, MFMA-bound): 256 x 256 tiles, eight waves of 128 x 64;
+// the row tiles of one vocab tile get consecutive logical ids on one XCD, so
+// the weight tile they share is read from HBM once and then hit in L2.
 //
 // lm_head_stream (129..256 rows, the weight-streaming regime):
 //  * Every row of the padded row set is in one workgroup, so W is read from
@@ -24,9 +25,10 @@
 //    leaves the sum unchanged and makes a lane's 64 bytes per stage contiguous.
 //  * The gathered hidden rows (the operand the four waves share) are staged
 //    per 64-wide k-stage in double-buffered LDS.
-//  * One persistent workgroup per CU walks its tiles over a flattened
-//    (tile, k-stage) index, so prefetch runs across tile boundaries and the
-//    1187 vocab tiles (a prime count for V = 151936) spread within one tile.
+//  * Persistent workgroups (one or two per CU) walk their tiles over a
+//    flattened (tile, k-stage) index, so prefetch runs across tile boundaries
+//    and the 1187 vocab tiles (a prime count for V = 151936) spread within one
+//    tile.
 //
 // Every global load is unconditional: pad vocab ids and pad rows read a
 // clamped, in-bounds address and the outputs they pollute are never stored.
@@ -168,21 +170,21 @@ __global__ __launch_bounds__(kThreads) void lm_head_tiled(Params p) {
 
 
 // ---------------------------------------------------------------------------
-// persistent weight-streaming kernel: one workgroup per CU
+// persistent weight-streaming kernel: OCC workgroups per CU
 // ---------------------------------------------------------------------------
-// A workgroup tile is 128*VW vocab ids x all (padded) rows.  The hidden rows
-// are the operand shared by the whole tile and are re-read from L2 once per
-// tile, so wide tiles (VW = 2: 256 ids) halve that traffic.  Each CU runs one
-// workgroup that walks tiles blockIdx.x, blockIdx.x + gridDim.x, ... over a
-// flattened (tile, k-stage) index: W and hidden are prefetched P stages ahead
-// straight across tile boundaries, and the tiles per CU differ by at most one
-// (a CU with deep prefetch can pull well above its fair share of HBM, so the
-// last, partial round still streams at full rate).  The LDS is padded so that
-// no second workgroup fits a CU.
-template <int MB, int VW, int P>
-__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_head_stream(Params p) {
+// A workgroup tile is 128*VW vocab ids x all (padded) rows; the hidden rows
+// are the operand the whole tile shares and are re-read from L2 once per
+// tile.  Each of the OCC * (CU count) workgroups walks tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ... over a flattened (tile, k-stage) index: W is
+// prefetched P stages ahead straight across tile boundaries, and the tiles
+// per workgroup differ by at most one.  With OCC = 1 the LDS is padded so that
+// no second workgroup fits a CU; with OCC = 2 two workgroups share each CU, so
+// one's LDS and barrier waits overlap the other's MFMAs.
+template <int MB, int VW, int P, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void lm_head_stream(Params p) {
   constexpr int MP = MB * 32;
-  constexpr int MPA = MP > 288 ? MP : 288;  // LDS rows allocated (>= 81 KB: one workgroup per CU)
+  // LDS rows allocated: with OCC = 1, at least 81 KB, so that one workgroup fills a CU
+  constexpr int MPA = (OCC == 1 && MP < 288) ? 288 : MP;
   constexpr int SK = 64;
   constexpr int LDH = SK + 8;
   constexpr int TV = 128 * VW;  // vocab ids per tile
@@ -328,24 +330,176 @@ int cu_count() {
   return cus[dev];
 }
 
-template <int MB, int VW, int P>
+template <int MB, int VW, int P, int OCC = 1>
 hipError_t launch_stream(const Params& p, hipStream_t stream) {
   if ((p.D / 64) % P != 0) return hipErrorInvalidValue;
   const int ntiles = (p.V + 128 * VW - 1) / (128 * VW);
-  const int grid = min(ntiles, cu_count());
-  hipLaunchKernelGGL((lm_head_stream<MB, VW, P>), dim3(grid), dim3(kThreads), 0, stream, p);
+  const int grid = min(ntiles, OCC * cu_count());
+  hipLaunchKernelGGL((lm_head_stream<MB, VW, P, OCC>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int P>
-hipError_t launch_stream_m(const Params& p, hipStream_t stream) {
+// 129..256 rows.  Up to 160 rows two workgroups share a CU (2-stage prefetch,
+// registers for two waves per SIMD); above that one workgroup per CU.
+hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
+  const int ks = p.D / 64;
   switch ((p.M + 31) / 32) {
-    case 5: return launch_stream<5, 1, P>(p, stream);
-    case 6: return launch_stream<6, 1, P>(p, stream);
-    case 7: return launch_stream<7, 1, (P > 2 ? 2 : P)>(p, stream);
-    case 8: return launch_stream<8, 1, (P > 2 ? 2 : P)>(p, stream);
-    default: return hipErrorInvalidValue;
+    case 5:
+      if (ks % 2 == 0) return launch_stream<5, 1, 2, 2>(p, stream);
+      return launch_stream<5, 1, 1, 2>(p, stream);
+    case 6:
+      if (ks % 4 == 0) return launch_stream<6, 1, 4, 1>(p, stream);
+      if (ks % 2 == 0) return launch_stream<6, 1, 2, 1>(p, stream);
+      return launch_stream<6, 1, 1, 1>(p, stream);
+    case 7:
+      if (ks % 2 == 0) return launch_stream<7, 1, 2, 1>(p, stream);
+      return launch_stream<7, 1, 1, 1>(p, stream);
+    case 8:
+      if (ks % 2 == 0) return launch_stream<8, 1, 2, 1>(p, stream);
+      return launch_stream<8, 1, 1, 1>(p, stream);
+    default:
+      return hipErrorInvalidValue;
   }
+}
+
+// ---------------------------------------------------------------------------
+// large-tile kernel for many rows (the MFMA-bound regime)
+// ---------------------------------------------------------------------------
+// Tile 256 vocab x 256 rows x 64 k, eight waves as 2 (vocab) x 4 (rows) of
+// 128 x 64, two waves per SIMD so that one wave's LDS traffic and barrier
+// waits overlap the other's MFMAs; double-buffered LDS (one workgroup per CU)
+// with the next k-tile prefetched into registers, and the fragments of the
+// next k-step read while the current one's MFMAs run.  A wave reads 3/4 KB of
+// LDS per MFMA (1 KB for the 64 x 64 wave tiles of lm_head_tiled).
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_big8(Params p) {
+  constexpr int NT = 512;
+  constexpr int TVB = 256, BR = 256;
+  constexpr int NA = 4, NB = 2;           // 32-blocks per wave: 128 vocab x 64 rows
+  constexpr int CA = TVB * 8 / NT;        // 4 chunks of W per thread per k-tile
+  constexpr int CB = BR * 8 / NT;         // 4 of hidden
+  __shared__ unsigned short ws[2][TVB][LDK];
+  __shared__ unsigned short hs[2][BR][LDK];
+
+  const int mtiles = (p.M + BR - 1) / BR;
+  const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int mt = lid % mtiles;
+  const int vt = lid / mtiles;
+  const int v0 = vt * TVB;
+  const int m0 = mt * BR;
+  const int t = threadIdx.x;
+  const int lane = t % kWave;
+  const int wave = t / kWave;
+  const int half = lane / 32;
+  const int col = lane % 32;
+  const int wv = wave / 4;  // vocab half
+  const int wm = wave % 4;  // row quarter
+
+  const unsigned short* wsrc[CA];
+  const unsigned short* hsrc[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int c = t + NT * i;
+    const int v = min(v0 + c / 8, p.V - 1);
+    wsrc[i] = p.w + (size_t)v * p.D + (c % 8) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = t + NT * i;
+    const int m = min(m0 + c / 8, p.M - 1);
+    const int hr = min(max(p.rows[m], 0), p.R - 1);  // never leave hidden
+    hsrc[i] = p.hidden + (size_t)hr * p.D + (c % 8) * 8;
+  }
+  u32x4 wreg[CA], hreg[CB];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) wreg[i] = ld16(wsrc[i] + k0);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) hreg[i] = ld16(hsrc[i] + k0);
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int c = t + NT * i;
+      st16(&ws[buf][c / 8][(c % 8) * 8], wreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = t + NT * i;
+      st16(&hs[buf][c / 8][(c % 8) * 8], hreg[i]);
+    }
+  };
+  floatx16 acc[NA][NB];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[a][b] = floatx16{};
+
+  const int ksteps = p.D / BK;
+  const int klast = (ksteps - 1) * BK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int buf = ks & 1;
+    fetch(min((ks + 1) * BK, klast));  // past the end: re-reads the last tile (L2 hit)
+    u32x4 fa[2][NA], fb[2][NB];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) fa[0][a] = ld16(&ws[buf][wv * 128 + a * 32 + col][half * 8]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) fb[0][b] = ld16(&hs[buf][wm * 64 + b * 32 + col][half * 8]);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+          fa[cur ^ 1][a] = ld16(&ws[buf][wv * 128 + a * 32 + col][(kk + 1) * 16 + half * 8]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          fb[cur ^ 1][b] = ld16(&hs[buf][wm * 64 + b * 32 + col][(kk + 1) * 16 + half * 8]);
+      }
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[cur][a]), as_bf16x8(fb[cur][b]),
+                                                               acc[a][b], 0, 0, 0);
+    }
+    stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane holds vocab v0 + wv*128 + a*32 + 8*(r/4) + 4*half + r%4 of row m0 + wm*64 + b*32 + col
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int m = m0 + wm * 64 + b * 32 + col;
+    if (m >= p.M) continue;
+    float* out = p.logits + (size_t)m * p.V;
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int v = v0 + wv * 128 + a * 32 + 8 * q4 + 4 * half;
+        const float4 val = make_float4(acc[a][b][4 * q4], acc[a][b][4 * q4 + 1], acc[a][b][4 * q4 + 2],
+                                       acc[a][b][4 * q4 + 3]);
+        if (v + 3 < p.V && (p.V % 4) == 0) {
+          *(float4*)(out + v) = val;
+        } else {
+          if (v + 0 < p.V) out[v + 0] = val.x;
+          if (v + 1 < p.V) out[v + 1] = val.y;
+          if (v + 2 < p.V) out[v + 2] = val.z;
+          if (v + 3 < p.V) out[v + 3] = val.w;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_big8(const Params& p, hipStream_t stream) {
+  const int vt = (p.V + 255) / 256;
+  const int mt = (p.M + 255) / 256;
+  hipLaunchKernelGGL(lm_head_big8, dim3(vt * mt), dim3(512), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_tiled(const Params& p, hipStream_t stream) {
@@ -369,16 +523,11 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   p.R = R;
   p.vt = (V + BV - 1) / BV;
   p.mt = (M + BM - 1) / BM;
-  // One 128-row tile: the tiled kernel.  129..256 rows: stream the weight
-  // once past every row (the tiled kernel would run two row tiles).
-  if (M <= BM || M > kStreamRows) return launch_tiled(p, stream);
-  // Prefetch depth: 4 stages while the registers allow it (up to 192 rows),
-  // else 2; it must divide the number of 64-wide k-stages.
-  const int ks = D / 64;
-  const int want = M <= 192 ? 4 : 2;
-  if (want == 4 && ks % 4 == 0) return launch_stream_m<4>(p, stream);
-  if (ks % 2 == 0) return launch_stream_m<2>(p, stream);
-  return launch_stream_m<1>(p, stream);
+  // Up to 128 rows (one row tile): the tiled kernel.  129..256 rows: stream
+  // the weight once past every row.  More rows: the large-tile kernel.
+  if (M <= BM) return launch_tiled(p, stream);
+  if (M <= kStreamRows) return launch_stream_rows(p, stream);
+  return launch_big8(p, stream);
 }
 
 }  // namespace sfv
