@@ -7,7 +7,8 @@ draft-tree match, with all inputs resident in HBM.  Prints one JSON line.
     python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
 
 value = B1*N branch-tokens verified per step / seconds per step, over K steps
-in which the attention (independent of the rest) runs on a second stream.  A
+replayed from a HIP graph of one step, in which the attention (independent of
+the rest) runs on a second stream.  A
 second pass of K steps issued in order on one stream times each call with HIP
 events on the stream it runs on; the roofline object reports the dominant
 kernel (the LM head) from those against the HBM peak, with the HBM traffic
@@ -43,6 +44,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the attention in order on the main stream instead of beside the LM head")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="issue the timed steps call by call instead of replaying a HIP graph")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the steps, run 3 plain device copies of this many bytes "
                          "(the calibration kernel for the HBM byte counters)")
@@ -150,10 +155,19 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K whole steps (attention overlapped with the rest on a
-    # second stream, joined inside each step), bracketed by synchronize.
+    # second stream, joined inside each step), replayed from a HIP graph of
+    # one step unless --no-graph, bracketed by synchronize.
+    if not a.no_graph:
+        step.capture(xd, overlap=not a.no_overlap)
+        for _ in range(2):
+            step.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(a.steps):
-        step.run(xd)
+        if a.no_graph:
+            step.run(xd, overlap=not a.no_overlap)
+        else:
+            step.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -196,7 +210,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B1": wl.B1, "N": wl.N, "L": wl.L, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "d": wl.d, "D": wl.D, "V": wl.V, "masked_rows": M,
-                   "temperature": wl.T, "parallelism": "none (1 GPU)"},
+                   "temperature": wl.T, "parallelism": "none (1 GPU)",
+                   "launch": "call by call" if a.no_graph else "hip graph",
+                   "attention": "in order" if a.no_overlap else "beside the LM head"},
         "roofline": {"bound": "hbm", "kernel": "lm_head", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,

@@ -58,6 +58,7 @@ class VerifyStep:
         self.n_accepted = torch.empty(1, dtype=torch.int32, device=dev)
         self.status = torch.empty(1, dtype=torch.int32, device=dev)
         self._side = None  # second stream for the attention (created on first overlapped run)
+        self._graph = None
 
     # the individual rows of the hot path -----------------------------------
     def attend(self, x, stream=None):
@@ -110,6 +111,26 @@ class VerifyStep:
         self.match(x, main)
         self._join.record(self._side)
         main.wait_event(self._join)
+
+    def capture(self, x, overlap=True):
+        """Capture one whole step (both streams) in a HIP graph; replay() then
+        launches it with one call.  The graph holds the current buffers and
+        inputs: replays recompute the same step."""
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            self.run(x, stream=cap, overlap=overlap)  # warm the side stream and events outside capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            self.run(x, stream=cap, overlap=overlap)
+        torch.cuda.synchronize()
+        self._graph = g
+        return g
+
+    def replay(self):
+        self._graph.replay()
 
     def results(self) -> dict:
         torch.cuda.synchronize()

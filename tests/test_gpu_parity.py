@@ -165,6 +165,40 @@ def test_full_step_parity(gpu_lib, idx):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("idx", [2, 3])
+def test_graph_replay_matches_eager(gpu_lib, idx):
+    """The whole step captured in a HIP graph: every replay (with eager work and
+    synchronisation between replays, and the outputs overwritten before each)
+    reproduces the eager step bit for bit."""
+    wl = synth.WORKLOADS[idx]
+    say(f"graph replay, workload {idx}")
+    x = host_inputs(idx)
+    xd = to_device(x)
+    step = step_for(wl, x)
+    step.run(xd)
+    ref = {k: (v.clone() if torch.is_tensor(v) else np.copy(v) if isinstance(v, np.ndarray) else v)
+           for k, v in step.results().items()}
+    step.capture(xd)
+    outs = [step.o, step.lse, step.logits, step.next_state, step.commit_pos, step.token, step.conf,
+            step.chain, step.n_accepted, step.status, step.rows, step.count]
+    for rep in range(3):
+        for t in outs:  # eager work between replays: poison every output
+            t.fill_(-7 if not t.is_floating_point() else float("nan"))
+        torch.cuda.synchronize()
+        step.replay()
+        got = step.results()
+        for k, a in ref.items():
+            b = got[k]
+            if torch.is_tensor(a):
+                assert torch.equal(a, b), f"replay {rep}: {k} differs from the eager step"
+            elif isinstance(a, np.ndarray):
+                assert np.array_equal(a, b), f"replay {rep}: {k} differs from the eager step"
+            else:
+                assert a == b, (rep, k)
+    del xd, step
+    torch.cuda.empty_cache()
+
+
 def test_selfcheck_bounds(gpu_lib):
     out = torch.zeros(2, dtype=torch.float64, device="cuda")
     say("self-check: all 2^32 noise words and all fp32 exp2 arguments in [-126, 0]")
