@@ -178,7 +178,6 @@ int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* s
                uint64_t step0, int64_t pos0, int k_max, float tau, int32_t* next_state,
                int32_t* commit_pos, int32_t* token, float* conf, void* workspace,
                size_t workspace_bytes, void* stream) {
-  (void)tau;
   int rc = check_commit_dims(B1, N, M, V);
   if (rc != SFV_OK) return rc;
   if (!state || !next_state || !commit_pos || !workspace) return fail(SFV_E_INVAL, "null pointer");
@@ -187,7 +186,8 @@ int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* s
     return fail(SFV_E_INVAL, "temperature must be finite and >= 0");
   }
   if (k_max < 1) return fail(SFV_E_INVAL, "k_max=%d < 1", k_max);
-  if (k_max != 1) return fail(SFV_E_UNSUPPORTED, "k_max=%d: only one position per step", k_max);
+  if (k_max > N) return fail(SFV_E_INVAL, "k_max=%d > N=%d", k_max, N);
+  if (k_max > 1 && !std::isfinite(tau)) return fail(SFV_E_INVAL, "tau must be finite");
   if ((uintptr_t)logits % 16 != 0) return fail(SFV_E_INVAL, "logits must be 16-byte aligned");
   sfv::TreeArgs tree;
   rc = make_tree(parent_host, B1, &tree);
@@ -199,7 +199,8 @@ int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* s
     return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
   }
   return hip_status(sfv::launch_commit(logits, rows, M, state, tree, N, V, temperature, seed, step0,
-                                       pos0, next_state, commit_pos, token, conf, workspace, plan,
+                                       pos0, k_max, tau, next_state, commit_pos, token, conf,
+                                       workspace, plan,
                                        (hipStream_t)stream),
                     "sfv_commit");
 }

@@ -514,6 +514,8 @@ struct FinArgs {
   int32_t* token;
   float* conf;
   int M, N, V, splits;
+  int k_max;
+  float tau;
   bool noisy;
 };
 
@@ -527,6 +529,11 @@ __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, Ws
   __shared__ int sCand[kMaxBlock];
   __shared__ double red[kThreads / kWave];
   __shared__ int best_n_s, ncand_s;
+  __shared__ double sX[kMaxBlock];  // S used for the ranking (exact where an interval is ambiguous)
+  __shared__ int sNeed[kMaxBlock];
+  __shared__ int sSel[kMaxBlock];
+  __shared__ double sU;
+  static_assert(kMaxBlock <= kThreads, "one thread per position below");
 
   const int i = blockIdx.x;
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
@@ -613,35 +620,119 @@ __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, Ws
     }
   }
   __syncthreads();
-  int best = best_n_s;
-  if (ncand_s > 1) {
-    // re-decide exactly: S summed with fp64 exp in a fixed order
-    double bestS = 0.0;
-    best = -1;
-    for (int c = 0; c < ncand_s; ++c) {
-      const int n = sCand[c];
-      const float* src = a.logits + (size_t)lmap[n] * a.V;
-      const double M = (double)sM[n];
-      double s = 0.0;
-      for (int v = t; v < a.V; v += kThreads) s += exp((double)src[v] - M);
+
+  // Exact S of position n: fp64 exp summed in a fixed order by the workgroup.
+  auto exact_S = [&](int n) -> double {
+    const float* src = a.logits + (size_t)lmap[n] * a.V;
+    const double M = (double)sM[n];
+    double s = 0.0;
+    for (int v = t; v < a.V; v += kThreads) s += exp((double)src[v] - M);
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
-      if (lane == 0) red[wave] = s;
-      __syncthreads();
-      double tot = 0.0;
-      for (int w = 0; w < kThreads / kWave; ++w) tot += red[w];
-      __syncthreads();
-      if (best < 0 || tot < bestS) {
-        best = n;
-        bestS = tot;
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    double tot = 0.0;
+    for (int w = 0; w < kThreads / kWave; ++w) tot += red[w];
+    __syncthreads();
+    return tot;
+  };
+
+  if (a.k_max == 1) {
+    int best = best_n_s;
+    if (ncand_s > 1) {  // re-decide exactly among the overlapping intervals
+      double bestS = 0.0;
+      best = -1;
+      for (int c = 0; c < ncand_s; ++c) {
+        const int n = sCand[c];
+        const double tot = exact_S(n);
+        if (best < 0 || tot < bestS) {
+          best = n;
+          bestS = tot;
+        }
       }
     }
+    for (int n = t; n < N; n += kThreads) {
+      const int f = f0 + n;
+      a.next_state[f] = (n == best) ? sTok[n] : a.state[f];
+    }
+    if (t == 0) a.commit_pos[i] = best;
+    return;
   }
+
+  // Threshold commit of up to k_max positions (SpecFold, evaluation setup,
+  // "Models and baselines": the decoders unmask the positions whose
+  // confidence clears a threshold, 0.9 there): in
+  // (S ascending, position ascending) order, the first position, then the
+  // following ones while fewer than k_max are taken and fl32(1/S) >= tau.
+  // Candidates are the positions whose interval [S - E, S + E] starts at or
+  // below U, the k_max-th smallest upper end: no other can be among the first
+  // k_max.  A candidate gets its exact S when its interval overlaps another
+  // candidate's or when its two ends fall on different sides of tau.
+  const bool mk = t < N && sS[t] >= 0.0;
+  const double lo = mk ? sS[t] - (double)sE[t] : 0.0;
+  const double hi = mk ? sS[t] + (double)sE[t] : 0.0;
+  const int nm = __syncthreads_count(mk);
+  const int kk = min(a.k_max, nm);
+  if (mk) {
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+      if (m == t || sS[m] < 0.0) continue;
+      const double hm = sS[m] + (double)sE[m];
+      rank += (hm < hi || (hm == hi && m < t));
+    }
+    if (rank == kk - 1) sU = hi;
+  }
+  __syncthreads();
+  const double U = nm > 0 ? sU : 0.0;
+  const bool inC = mk && lo <= U;
+  if (t < kMaxBlock) {
+    bool need = false;
+    if (inC) {
+      for (int m = 0; m < N; ++m) {
+        if (m == t || sS[m] < 0.0) continue;
+        const double lm = sS[m] - (double)sE[m], hm = sS[m] + (double)sE[m];
+        if (lm <= U && lo <= hm && lm <= hi) need = true;
+      }
+      const bool c_lo = (float)(1.0 / hi) >= a.tau;  // confidence at the interval's ends
+      const bool c_hi = (float)(1.0 / lo) >= a.tau;
+      if (c_lo != c_hi) need = true;
+    }
+    sNeed[t] = need;
+    sSel[t] = 0;
+    sX[t] = mk ? sS[t] : -1.0;
+  }
+  __syncthreads();
+  for (int n = 0; n < N; ++n) {  // uniform: every thread reads the same flags
+    if (!sNeed[n]) continue;
+    const double e = exact_S(n);
+    if (t == 0) sX[n] = e;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int taken = 0;
+    while (taken < kk) {
+      int bn = -1;
+      double bs = 0.0;
+      for (int n = 0; n < N; ++n) {
+        if (sS[n] < 0.0 || sSel[n] || sS[n] - (double)sE[n] > U) continue;
+        if (bn < 0 || sX[n] < bs) {
+          bn = n;
+          bs = sX[n];
+        }
+      }
+      if (bn < 0) break;
+      if (taken > 0 && !((float)(1.0 / bs) >= a.tau)) break;
+      sSel[bn] = 1;
+      a.commit_pos[i * a.k_max + taken] = bn;
+      ++taken;
+    }
+    for (int j = taken; j < a.k_max; ++j) a.commit_pos[i * a.k_max + j] = -1;
+  }
+  __syncthreads();
   for (int n = t; n < N; n += kThreads) {
     const int f = f0 + n;
-    a.next_state[f] = (n == best) ? sTok[n] : a.state[f];
+    a.next_state[f] = sSel[n] ? sTok[n] : a.state[f];
   }
-  if (t == 0) a.commit_pos[i] = best;
 }
 
 // ---------------------------------------------------------------------------
@@ -712,7 +803,8 @@ hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows
 
 hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
                          const TreeArgs& tree, int N, int V, float temperature, uint64_t seed,
-                         uint64_t step0, int64_t pos0, int32_t* next_state, int32_t* commit_pos,
+                         uint64_t step0, int64_t pos0, int k_max, float tau, int32_t* next_state,
+                         int32_t* commit_pos,
                          int32_t* token, float* conf, void* ws_base, const CommitPlan& plan,
                          hipStream_t stream) {
   const bool noisy = temperature > 0.f;
@@ -756,6 +848,8 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
   fa.N = N;
   fa.V = V;
   fa.splits = plan.splits;
+  fa.k_max = k_max;
+  fa.tau = tau;
   fa.noisy = noisy;
   hipLaunchKernelGGL(commit_finalize_kernel, dim3(tree.B1), dim3(kThreads), 0, stream, fa, ws);
   return hipGetLastError();

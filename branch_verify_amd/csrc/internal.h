@@ -54,7 +54,8 @@ CommitPlan commit_plan(int B1, int N, int M, int V, int items_max, bool noisy);
 
 hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
                          const TreeArgs& tree, int N, int V, float temperature, uint64_t seed,
-                         uint64_t step0, int64_t pos0, int32_t* next_state, int32_t* commit_pos,
+                         uint64_t step0, int64_t pos0, int k_max, float tau, int32_t* next_state,
+                         int32_t* commit_pos,
                          int32_t* token, float* conf, void* ws, const CommitPlan& plan,
                          hipStream_t stream);
 

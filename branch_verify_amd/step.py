@@ -32,13 +32,14 @@ class VerifyStep:
     """Buffers and calls of one multi-branch verification step of fixed shape."""
 
     def __init__(self, B1, N, L, Hq, Hkv, d, D, V, M, parent, temperature, seed, step0, pos0,
-                 S_max=-1, device="cuda"):
+                 S_max=-1, k_max=1, tau=0.0, device="cuda"):
         sfv.load()
         self.B1, self.N, self.L, self.Hq, self.Hkv, self.d = B1, N, L, Hq, Hkv, d
         self.D, self.V, self.M = D, V, M
         self.parent = [int(x) for x in parent]
         self.T, self.seed, self.step0, self.pos0 = float(temperature), seed, step0, pos0
         self.S_max = S_max
+        self.k_max, self.tau = int(k_max), float(tau)
         self.scale = 1.0 / math.sqrt(d)
         dev = device
         self.o = torch.empty((B1, N, Hq, d), dtype=torch.bfloat16, device=dev)
@@ -51,7 +52,7 @@ class VerifyStep:
         self.commit_ws_bytes = sfv.sfv_commit_workspace_bytes(B1, N, M, V)
         self.commit_ws = torch.empty(max(1, self.commit_ws_bytes), dtype=torch.uint8, device=dev)
         self.next_state = torch.empty((B1, N), dtype=torch.int32, device=dev)
-        self.commit_pos = torch.empty((B1, 1), dtype=torch.int32, device=dev)
+        self.commit_pos = torch.empty((B1, self.k_max), dtype=torch.int32, device=dev)
         self.token = torch.empty(max(1, M), dtype=torch.int32, device=dev)
         self.conf = torch.empty(max(1, M), dtype=torch.float32, device=dev)
         self.chain = torch.empty(B1, dtype=torch.int32, device=dev)
@@ -76,12 +77,12 @@ class VerifyStep:
     def commit(self, x, logits=None, stream=None):
         sfv.sfv_commit(self.logits if logits is None else logits, self.rows, self.M, x["state"],
                        self.parent, self.B1, self.N, self.V, self.T, self.seed, self.step0,
-                       self.pos0, 1, 0.0, self.next_state, self.commit_pos, self.token, self.conf,
+                       self.pos0, self.k_max, self.tau, self.next_state, self.commit_pos, self.token, self.conf,
                        self.commit_ws, self.commit_ws_bytes, stream)
 
     def match(self, x, stream=None):
         sfv.sfv_match_tree(x["state"], self.next_state, self.commit_pos, self.parent, self.B1,
-                           self.N, 1, self.S_max, self.chain, self.n_accepted, self.status, stream)
+                           self.N, self.k_max, self.S_max, self.chain, self.n_accepted, self.status, stream)
 
     def run(self, x, stream=None, overlap=True):
         """The whole hot path, stream-ordered, no host synchronisation.
@@ -143,9 +144,9 @@ class VerifyStep:
             h=int(self.n_accepted.item()), status=int(self.status.item()))
 
 
-def step_for(wl, inp: dict, device="cuda", S_max=None) -> VerifyStep:
+def step_for(wl, inp: dict, device="cuda", S_max=None, k_max=1, tau=0.0) -> VerifyStep:
     from .synth import masked_count
     M = masked_count(inp["state"])
     return VerifyStep(wl.B1, wl.N, wl.L, wl.Hq, wl.Hkv, wl.d, wl.D, wl.V, M, inp["parent"], wl.T,
                       wl.seed, wl.step0, wl.pos0, S_max=wl.S_t if S_max is None else S_max,
-                      device=device)
+                      k_max=k_max, tau=tau, device=device)

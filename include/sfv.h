@@ -123,15 +123,22 @@ int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R,
  *           the noise of a position.
  *   S = sum_v exp(l_v - max l) (fp64 decision); conf = fl32(1/S) (fp32 fast
  *   path, relative error below 1e-5).
- * Per branch: the masked position with the smallest S (ties: lowest n) is
- * committed: next_state[i][n*] = token; commit_pos[i][0] = n*, or -1 when the
- * branch has no masked position.  k_max must be 1 (tau is ignored).
+ * Per branch, masked positions are ranked by S ascending (ties: lowest n).
+ * The first is committed; after it, further positions in that order while
+ * fewer than k_max are taken and fl32(1/S) >= tau, stopping at the first that
+ * fails (SpecFold, evaluation setup, "Models and baselines": confidence-
+ * threshold unmasking).  next_state[i][n] = token
+ * for each committed n, else state[i][n]; commit_pos[i][0..k_max) = the
+ * committed positions in rank order, -1 padded (all -1 when the branch has no
+ * masked position).  With k_max = 1, tau is ignored.  Where the fp32 bound on
+ * S leaves the ranking or a tau decision open, S is recomputed in fp64.
  *
  *   logits [M][V] fp32; rows [M] int32 = sfv_masked_rows(state) order
  *   state, next_state [B1][N] int32; parent_host [B1] host int32, parent[0] = -1
  *   commit_pos [B1][k_max] int32; token [M] int32; conf [M] fp32
  *   workspace: sfv_commit_workspace_bytes(B1, N, M, V) bytes
- * Supported: V % 8 == 0, V < 2^31 / 8, T >= 0 and finite.
+ * Supported: V % 8 == 0, V < 2^31 / 8, T >= 0 and finite, 1 <= k_max <= N,
+ * tau finite when k_max > 1.
  */
 int sfv_commit_workspace_bytes(int B1, int N, int M, int V, size_t* bytes);
 int sfv_commit(const float* logits, const int32_t* rows, int M,

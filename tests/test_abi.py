@@ -86,7 +86,8 @@ def test_lm_head_validation(lib):
     assert lib.sfv_lm_head(P(0x1004), f, 4, 8, f, 128, 512, f, None) == sfv.SFV_E_INVAL
 
 
-def _commit(lib, parent, B1=3, N=8, M=4, V=512, T=0.0, k_max=1, ws_bytes=None, logits=0x1000):
+def _commit(lib, parent, B1=3, N=8, M=4, V=512, T=0.0, k_max=1, ws_bytes=None, logits=0x1000,
+            tau=0.0):
     P = ctypes.c_void_p
     f = P(0x1000)
     par = (ctypes.c_int32 * len(parent))(*parent)
@@ -94,7 +95,7 @@ def _commit(lib, parent, B1=3, N=8, M=4, V=512, T=0.0, k_max=1, ws_bytes=None, l
         ws_bytes = 1 << 30
     return lib.sfv_commit(P(logits), f, M, f, ctypes.cast(par, P), B1, N, V, ctypes.c_float(T),
                           ctypes.c_uint64(1), ctypes.c_uint64(2), ctypes.c_int64(3), k_max,
-                          ctypes.c_float(0.0), f, f, f, f, f, ws_bytes, None)
+                          ctypes.c_float(tau), f, f, f, f, f, ws_bytes, None)
 
 
 def test_commit_validation(lib):
@@ -106,7 +107,9 @@ def test_commit_validation(lib):
     assert _commit(lib, [-1, 0, 1], T=-1.0) == sfv.SFV_E_INVAL
     assert _commit(lib, [-1, 0, 1], T=float("nan")) == sfv.SFV_E_INVAL
     assert _commit(lib, [-1, 0, 1], k_max=0) == sfv.SFV_E_INVAL
-    assert _commit(lib, [-1, 0, 1], k_max=2) == sfv.SFV_E_UNSUPPORTED
+    assert _commit(lib, [-1, 0, 1], k_max=9) == sfv.SFV_E_INVAL  # more than N positions
+    assert _commit(lib, [-1, 0, 1], k_max=2, tau=float("nan")) == sfv.SFV_E_INVAL
+    assert _commit(lib, [-1, 0, 1], k_max=2, tau=float("inf")) == sfv.SFV_E_INVAL
     assert _commit(lib, [-1, 0, 1], ws_bytes=16) == sfv.SFV_E_WORKSPACE
     assert _commit(lib, [-1, 0, 1], logits=0x1004) == sfv.SFV_E_INVAL
     assert _commit(lib, [-1] + [0] * 64, B1=65) == sfv.SFV_E_INVAL

@@ -110,12 +110,14 @@ def check_lm_head(x, res, full):
 # ---------------------------------------------------------------------------
 # commit and match
 # ---------------------------------------------------------------------------
-def check_commit_match(x, res, wl_T, seed, step0, pos0, S_max, logits_host=None):
+def check_commit_match(x, res, wl_T, seed, step0, pos0, S_max, logits_host=None, k_max=1, tau=0.0):
     rows = res["rows"]
     lg = res["logits"].cpu().numpy() if logits_host is None else logits_host
-    nxt, cpos, tok, conf, S = O.commit(lg, rows, x["state"], x["parent"], wl_T, seed, step0, pos0)
+    nxt, cpos, tok, conf, S = O.commit(lg, rows, x["state"], x["parent"], wl_T, seed, step0, pos0,
+                                       k_max=k_max, tau=tau)
     assert np.array_equal(res["token"], tok), np.flatnonzero(res["token"] != tok)[:10]
-    assert np.array_equal(res["commit_pos"][:, 0], cpos[:, 0])
+    assert res["commit_pos"].shape == cpos.shape
+    assert np.array_equal(res["commit_pos"], cpos), np.flatnonzero(np.any(res["commit_pos"] != cpos, 1))[:10]
     assert np.array_equal(res["next_state"], nxt)
     rel = np.max(np.abs(res["conf"].astype(np.float64) - conf.astype(np.float64)) / conf) if conf.size else 0.0
     say(f"commit tokens/positions exact; conf max rel err {rel:.2e}")
@@ -213,7 +215,7 @@ def test_selfcheck_bounds(gpu_lib):
 # ---------------------------------------------------------------------------
 # commit + match on planted trees (toy target; SPOT Propositions 1-2)
 # ---------------------------------------------------------------------------
-def _planted_case(rng, N, V, T, step0, pos0, seed, depth, decoys):
+def _planted_case(rng, N, V, T, step0, pos0, seed, depth, decoys, k_max=1, tau=0.0):
     s0 = rng.integers(0, V, N).astype(np.int32)
     s0[rng.choice(N, max(depth + 2, N // 2), replace=False)] = O.MASK
     traj = [s0]
@@ -221,7 +223,7 @@ def _planted_case(rng, N, V, T, step0, pos0, seed, depth, decoys):
         cur = traj[-1][None]
         rows = O.masked_rows(cur)
         lg = synth.state_keyed_logits(seed, cur[0], V)[rows]
-        nxt, *_ = O.commit(lg, rows, cur, np.array([-1]), T, seed, step0 + t, pos0)
+        nxt, *_ = O.commit(lg, rows, cur, np.array([-1]), T, seed, step0 + t, pos0, k_max=k_max, tau=tau)
         traj.append(nxt[0])
     states, parent = [traj[0]], [-1]
     for t in range(1, len(traj)):
@@ -242,11 +244,12 @@ def _planted_case(rng, N, V, T, step0, pos0, seed, depth, decoys):
     return st, np.array(parent, dtype=np.int32), len(traj) - 1
 
 
-def _run_commit_match(st, parent, V, T, seed, step0, pos0, logits_host, S_max=1):
+def _run_commit_match(st, parent, V, T, seed, step0, pos0, logits_host, S_max=1, k_max=1, tau=0.0):
     B1, N = st.shape
     rows = O.masked_rows(st)
     M = rows.size
-    step = VerifyStep(B1, N, 0, 1, 1, 32, 64, V, M, parent, T, seed, step0, pos0, S_max=S_max)
+    step = VerifyStep(B1, N, 0, 1, 1, 32, 64, V, M, parent, T, seed, step0, pos0, S_max=S_max,
+                      k_max=k_max, tau=tau)
     xd = {"state": torch.from_numpy(st).cuda()}
     step.masked_rows(xd)
     lg = torch.from_numpy(np.ascontiguousarray(logits_host)).cuda()
@@ -409,3 +412,122 @@ def test_commit_nothing_masked(gpu_lib):
     assert np.array_equal(step.next_state.cpu().numpy(), st)
     assert np.all(step.commit_pos.cpu().numpy() == -1)
     assert int(step.n_accepted.item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# threshold commit of up to k_max positions per branch
+# ---------------------------------------------------------------------------
+def _spread_logits(rng, M, V):
+    """Rows of very different sharpness, so confidences spread from about 1/V
+    to about 1 and a threshold splits the ranked positions of a branch."""
+    scale = np.exp(rng.uniform(np.log(0.3), np.log(12.0), (M, 1)))
+    return (rng.standard_normal((M, V)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("k_max,q", [(2, 0.5), (3, 0.2), (4, 0.8), (8, 0.0), (5, 1.0)])
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_threshold_commit_random(gpu_lib, k_max, q, T):
+    rng = np.random.default_rng(k_max * 31 + int(10 * q))
+    B1, N, V = 9, 32, 4096
+    st = rng.integers(0, V, (B1, N)).astype(np.int32)
+    st[rng.random((B1, N)) < 0.6] = -1
+    st[3] = -1                  # fully masked branch
+    st[5, st[5] == -1] = 7      # nothing masked
+    parent = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, B1)], np.int32)
+    rows = O.masked_rows(st)
+    lg = _spread_logits(rng, rows.size, V)
+    *_, conf, _S = O.commit(lg, rows, st, parent, T, 4, 10, 0)
+    tau = float(np.quantile(conf, q))
+    say(f"threshold commit k_max={k_max} tau={tau:.4g} T={T}")
+    res = _run_commit_match(st, parent, V, T, 4, 10, 0, lg, S_max=-1, k_max=k_max, tau=tau)
+    check_commit_match(dict(state=st, parent=parent), res, T, 4, 10, 0, -1, logits_host=lg,
+                       k_max=k_max, tau=tau)
+    taken = np.sum(res["commit_pos"] >= 0, axis=1)
+    assert taken[5] == 0 and taken[3] >= 1
+
+
+def test_threshold_commit_tau_on_boundary(gpu_lib):
+    """tau equal to a position's fp32 confidence takes it (>=); one ulp above
+    does not: the fast path's bound straddles tau, so S is recomputed exactly."""
+    rng = np.random.default_rng(17)
+    B1, N, V = 4, 16, 8192
+    st = np.full((B1, N), -1, np.int32)
+    parent = np.array([-1, 0, 0, 1], np.int32)
+    rows = O.masked_rows(st)
+    lg = _spread_logits(rng, rows.size, V)
+    _n, cpos1, _t, conf, S = O.commit(lg, rows, st, parent, 0.0, 2, 3, 0, k_max=N, tau=-1e30)
+    for i in range(B1):
+        second = int(cpos1[i, 1])
+        c = np.float32(conf[i * N + second])  # rows are the whole block, in order
+        for tau, expect_two in ((float(c), True), (float(np.nextafter(c, np.float32(np.inf))), False)):
+            res = _run_commit_match(st, parent, V, 0.0, 2, 3, 0, lg, S_max=-1, k_max=2, tau=tau)
+            check_commit_match(dict(state=st, parent=parent), res, 0.0, 2, 3, 0, -1, logits_host=lg,
+                               k_max=2, tau=tau)
+            assert (res["commit_pos"][i, 1] == second) == expect_two
+
+
+def test_threshold_commit_ties_and_all(gpu_lib):
+    """Equal S (identical rows) rank by position; k_max = N with a very low tau
+    commits every masked position."""
+    rng = np.random.default_rng(23)
+    B1, N, V = 3, 12, 2048
+    st = np.full((B1, N), -1, np.int32)
+    st[1, ::3] = 5
+    parent = np.array([-1, 0, 1], np.int32)
+    rows = O.masked_rows(st)
+    lg = _spread_logits(rng, rows.size, V)
+    lg[4, 3] += 30.0                 # a very confident row ...
+    lg[[2, 5, 7, 9]] = lg[4]         # ... shared by five positions of branch 0
+    for k_max, tau in ((3, 0.0), (5, 0.5), (N, -1e30)):
+        say(f"ties k_max={k_max} tau={tau}")
+        res = _run_commit_match(st, parent, V, 0.0, 8, 8, 0, lg, S_max=-1, k_max=k_max, tau=tau)
+        check_commit_match(dict(state=st, parent=parent), res, 0.0, 8, 8, 0, -1, logits_host=lg,
+                           k_max=k_max, tau=tau)
+        if k_max == 3:
+            assert list(res["commit_pos"][0]) == [2, 4, 5]
+    assert np.all(res["next_state"] != -1)
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_threshold_planted_chain(gpu_lib, case):
+    """Drafts that each add up to k_max positions (the target's own threshold
+    commits) are matched hop by hop."""
+    rng = np.random.default_rng(700 + case)
+    N, V, seed, k_max = [16, 32, 64][case], [2048, 4096, 151936][case], 5 + case, [2, 3, 4][case]
+    T, tau = [0.0, 1.0, 0.7][case], [0.0, 1e-3, 0.5][case]
+    depth = int(rng.integers(2, 5))
+    st, parent, planted = _planted_case(rng, N, V, T, 40, 512, seed, depth, decoys=8,
+                                        k_max=k_max, tau=tau)
+    say(f"threshold planted case {case} B1={st.shape[0]} N={N} k_max={k_max} tau={tau} depth={depth}")
+    rows = O.masked_rows(st)
+    lg = np.stack([synth.state_keyed_logits(seed, st[r // N], V)[r % N] for r in rows])
+    res = _run_commit_match(st, parent, V, T, seed, 40, 512, lg, S_max=k_max, k_max=k_max, tau=tau)
+    h = check_commit_match(dict(state=st, parent=parent), res, T, seed, 40, 512, k_max,
+                           logits_host=lg, k_max=k_max, tau=tau)
+    assert h == planted
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_threshold_commit_workload(gpu_lib, idx):
+    """Threshold commit on the LM head's own logits at the full workload shape."""
+    wl = synth.WORKLOADS[idx]
+    x = host_inputs(idx)
+    xd = to_device(x)
+    step = step_for(wl, x, k_max=4, tau=0.0)
+    step.run(xd)
+    torch.cuda.synchronize()
+    res = step.results()
+    lg = res["logits"].cpu().numpy()
+    *_, conf, _S = O.commit(lg, res["rows"], x["state"], x["parent"], wl.T, wl.seed, wl.step0, wl.pos0)
+    for q in (0.0, 0.5, 0.9):
+        tau = float(np.quantile(conf, q))
+        step.tau = tau
+        say(f"workload {idx} threshold commit k_max=4 tau={tau:.4g}")
+        step.commit(xd)
+        step.match(xd)
+        torch.cuda.synchronize()
+        res = step.results()
+        check_commit_match(x, res, wl.T, wl.seed, wl.step0, wl.pos0, wl.S_t, logits_host=lg,
+                           k_max=4, tau=tau)
+    del xd, step
+    torch.cuda.empty_cache()
