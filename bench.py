@@ -189,6 +189,22 @@ def main():
 
     per = {n: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(a.steps)])) * 1e3
            for j, n in enumerate(names)}  # microseconds
+
+    # The threshold variant of the commit (up to k_max positions with
+    # confidence >= 0.9 per branch), on the same logits, timed the same way.
+    k_thr, tau_thr = max(2, wl.S_t), 0.9
+    thr = step_for(wl, x, k_max=k_thr, tau=tau_thr)
+    thr.masked_rows(xd)
+    tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    for s in range(a.steps):
+        tev[s][0].record(stream)
+        thr.commit(xd, logits=step.logits)
+        tev[s][1].record(stream)
+    torch.cuda.synchronize()
+    thr_us = float(np.mean([b.elapsed_time(e) for b, e in tev])) * 1e3
+    thr_taken = int((thr.commit_pos >= 0).sum().item())
+    del thr
     ms_per_step = elapsed / a.steps * 1e3
     alg = algorithmic(wl, M)
     lm_bytes, lm_flop = alg["lm_head"]
@@ -225,6 +241,9 @@ def main():
                                  "mfma_frac": af / (per["attention"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
     cb, _ = alg["commit"]
     out["commit_roofline"] = {"hbm_frac": cb / (per["commit"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    out["commit_threshold"] = {"k_max": k_thr, "tau": tau_thr, "us": thr_us,
+                               "positions_committed": thr_taken,
+                               "hbm_frac": cb / (thr_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
     if not a.no_cpu_baseline:
         note("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(wl, x)

@@ -21,7 +21,15 @@ Recipe (every tensor has its own numpy stream, so any subset can be drawn):
                                     positions, tokens U{0..V-1}
   streams [seed, 10..15]  q, k_blk, v_blk, k_ctx, v_ctx, hidden   N(0, 1)
   streams [seed, 16, c]   W rows in chunks of 4096                N(0, w_std)
+  streams [seed, 17, 18]  layer-input hidden states of the fold gate (below)
 All floats are drawn in fp32 and rounded to bfloat16 (round to nearest even).
+
+Layer-input hidden states for SpecFold's parent-child gate (Sec. 3.1
+Observation 1 and Fig. 6: a child's hidden state stays close to its
+parent's, with the divergence at masked and newly unmasked positions):
+H_0[n] ~ N(0, 1)^D; a draft's H_i[n] = H_par(i)[n] + sigma * N(0, 1)^D with
+sigma = 1 where the draft unmasked n, LogU(0.02, 0.5) where n is still
+masked, LogU(0.005, 0.05) where the parent already holds a token.
 """
 from __future__ import annotations
 
@@ -207,6 +215,29 @@ def draw_inputs(wl: Workload, seed: int | None = None, with_w: bool = True) -> d
     if with_w:
         inp["w"] = draw_w(wl, seed)
     return inp
+
+
+def draw_fold_hidden(wl: Workload, parent: np.ndarray, state: np.ndarray,
+                     seed: int | None = None) -> np.ndarray:
+    """bf16 bits [B1][N][D]: layer-input hidden states with the parent-child
+    structure described in the module docstring."""
+    seed = wl.seed if seed is None else seed
+    B1, N, D = wl.B1, wl.N, wl.D
+    rz = _rng(seed, 17)
+    rs = _rng(seed, 18)
+    H = np.empty((B1, N, D), dtype=np.float32)
+    H[0] = rz.standard_normal((N, D), dtype=np.float32)
+    H[0] = bf16_bits_to_f32(f32_to_bf16_bits(H[0]))
+    for i in range(1, B1):
+        p = int(parent[i])
+        fresh = (state[p] == MASK) & (state[i] != MASK)
+        masked = state[i] == MASK
+        sig = np.exp(rs.uniform(np.log(0.005), np.log(0.05), N))
+        sig = np.where(masked, np.exp(rs.uniform(np.log(0.02), np.log(0.5), N)), sig)
+        sig = np.where(fresh, 1.0, sig).astype(np.float32)
+        H[i] = H[p] + sig[:, None] * rz.standard_normal((N, D), dtype=np.float32)
+        H[i] = bf16_bits_to_f32(f32_to_bf16_bits(H[i]))
+    return f32_to_bf16_bits(H)
 
 
 def masked_count(state: np.ndarray) -> int:
