@@ -205,6 +205,31 @@ def main():
     thr_us = float(np.mean([b.elapsed_time(e) for b, e in tev])) * 1e3
     thr_taken = int((thr.commit_pos >= 0).sum().item())
     del thr
+
+    # SpecFold folded verification of the same batch's attention (delta 0.1):
+    # the gate on synthetic layer-input hidden states, then recomputed rows
+    # plus corrected folded rows; timed the same way as the dense attention.
+    from branch_verify_amd.step import folded_for
+    fold_delta = 0.1
+    h_layer = to_device({"h": synth.draw_fold_hidden(wl, x["parent"], x["state"])})["h"]
+    fa = folded_for(wl, x["parent"])
+    for _ in range(3):
+        fa.run(xd, h_layer, fold_delta)
+    torch.cuda.synchronize()
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    for s in range(a.steps):
+        fev[s][0].record(stream)
+        fa.gate(h_layer, fold_delta)
+        fev[s][1].record(stream)
+        fa.attend(xd)
+        fev[s][2].record(stream)
+    torch.cuda.synchronize()
+    gate_us = float(np.mean([e[0].elapsed_time(e[1]) for e in fev])) * 1e3
+    fattn_us = float(np.mean([e[1].elapsed_time(e[2]) for e in fev])) * 1e3
+    rec = fa.lists()["recompute"]
+    fold_ratio = float(1.0 - rec[1:].mean()) if wl.B1 > 1 else 0.0
+    gate_bytes = 2 * 2 * (wl.B1 - 1) * wl.N * wl.D + 4 * 5 * wl.B1 * wl.N
+    del fa, h_layer
     ms_per_step = elapsed / a.steps * 1e3
     alg = algorithmic(wl, M)
     lm_bytes, lm_flop = alg["lm_head"]
@@ -241,6 +266,10 @@ def main():
                                  "mfma_frac": af / (per["attention"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
     cb, _ = alg["commit"]
     out["commit_roofline"] = {"hbm_frac": cb / (per["commit"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    out["folded_attention"] = {"delta": fold_delta, "fold_ratio": fold_ratio, "gate_us": gate_us,
+                               "attention_us": fattn_us, "dense_attention_us": per["attention"],
+                               "speedup_vs_dense": per["attention"] / (gate_us + fattn_us),
+                               "gate_hbm_frac": gate_bytes / (gate_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
     out["commit_threshold"] = {"k_max": k_thr, "tau": tau_thr, "us": thr_us,
                                "positions_committed": thr_taken,
                                "hbm_frac": cb / (thr_us * 1e-6) / 1e9 / HBM_PEAK_GBS}

@@ -24,6 +24,7 @@ SOURCES = {
     "lm_head.hip": [],
     "commit.hip": ["-ffp-contract=off"],
     "match.hip": [],
+    "fold.hip": ["-ffp-contract=off"],
 }
 
 COMMON = [

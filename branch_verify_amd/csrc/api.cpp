@@ -134,6 +134,57 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk, con
                     "sfv_attend_branches");
 }
 
+int sfv_fold_gate(const void* hidden, const int32_t* parent_host, int B1, int N, int D, float delta,
+                  int32_t* recompute, int32_t* src, int32_t* rec_rows, int32_t* rec_count,
+                  int32_t* rec_pos, int32_t* branch_off, void* stream) {
+  sfv::TreeArgs tree;
+  const int rc = make_tree(parent_host, B1, &tree);
+  if (rc != SFV_OK) return rc;
+  if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
+  if (D < 8 || D % 8 != 0) return fail(SFV_E_UNSUPPORTED, "D=%d is not a positive multiple of 8", D);
+  if ((double)B1 * N * D > 2e9) return fail(SFV_E_INVAL, "hidden too large");
+  if (std::isnan(delta)) return fail(SFV_E_INVAL, "delta is NaN");
+  if (!hidden || !recompute || !src || !rec_rows || !rec_count || !rec_pos || !branch_off)
+    return fail(SFV_E_INVAL, "null pointer");
+  if ((uintptr_t)hidden % 16 != 0) return fail(SFV_E_INVAL, "hidden must be 16-byte aligned");
+  return hip_status(sfv::launch_fold_gate(hidden, tree, N, D, delta, recompute, src, rec_rows, rec_count,
+                                          rec_pos, branch_off, (hipStream_t)stream),
+                    "sfv_fold_gate");
+}
+
+int sfv_attend_folded_workspace_bytes(int B1, int N, int L, int Hq, int Hkv, int d, size_t* bytes) {
+  if (!bytes) return fail(SFV_E_INVAL, "bytes is NULL");
+  const int rc = check_attn_dims(B1, N, L, Hq, Hkv, d);
+  if (rc != SFV_OK) return rc;
+  *bytes = sfv::attn_plan(B1, N, L, Hq, Hkv, d).ws_bytes_folded;
+  return ok();
+}
+
+int sfv_attend_folded(const void* q, const void* k_blk, const void* v_blk, const void* k_ctx,
+                      const void* v_ctx, int B1, int N, int L, int Hq, int Hkv, int d, float softmax_scale,
+                      const int32_t* src, const int32_t* rec_rows, const int32_t* rec_count,
+                      const int32_t* rec_pos, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  const int rc = check_attn_dims(B1, N, L, Hq, Hkv, d);
+  if (rc != SFV_OK) return rc;
+  if (!q || !k_blk || !v_blk || !o || !lse || !src || !rec_rows || !rec_count || !rec_pos)
+    return fail(SFV_E_INVAL, "null pointer");
+  if (L > 0 && (!k_ctx || !v_ctx)) return fail(SFV_E_INVAL, "null context pointer with L=%d", L);
+  if (!std::isfinite(softmax_scale)) return fail(SFV_E_INVAL, "softmax_scale is not finite");
+  const sfv::AttnPlan plan = sfv::attn_plan(B1, N, L, Hq, Hkv, d);
+  if (workspace_bytes < plan.ws_bytes_folded) {
+    return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes_folded);
+  }
+  if (plan.ws_bytes_folded > 0 && !workspace) return fail(SFV_E_INVAL, "workspace is NULL");
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_blk | (uintptr_t)v_blk | (uintptr_t)k_ctx |
+                       (uintptr_t)v_ctx | (uintptr_t)o | (uintptr_t)workspace;
+  if (al % 16 != 0) return fail(SFV_E_INVAL, "tensor pointers must be 16-byte aligned");
+  return hip_status(sfv::launch_attention(q, k_blk, v_blk, k_ctx, v_ctx, B1, N, L, Hq, Hkv, d, softmax_scale,
+                                          o, lse, workspace, plan, (hipStream_t)stream, rec_rows, src, rec_count,
+                                          rec_pos),
+                    "sfv_attend_folded");
+}
+
 int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t* count, void* stream) {
   if (!state || !rows || !count) return fail(SFV_E_INVAL, "null pointer");
   if (B1 < 1 || B1 > SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "B1=%d not in [1, %d]", B1, SFV_MAX_BRANCHES);

@@ -19,6 +19,16 @@
 //    the tile; a key is visible to a row only if both belong to one branch.
 //  * Long contexts are split into key ranges (split-KV) whose (m, l, O)
 //    states are merged by log-sum-exp in a second kernel.
+//  * Folded verification (SpecFold App. A.1 and B) runs the same kernel in
+//    two more modes.  kCtx: only the compacted recomputed slots, against the
+//    context keys alone, leaving their (m, l, O) states in the workspace
+//    (workgroups past the live row count exit at once).  kBlock: every slot,
+//    with its resolved query (the source branch's at that position), against
+//    its own branch's block keys read through the slots' resolved sources;
+//    the epilogue merges in the context state of the slot's source row.  A
+//    folded slot's query equals its source's, and the context is shared, so
+//    the source's context state is exactly the folded row's: folded rows
+//    skip the context and nothing is subtracted.
 #include "common.h"
 #include "internal.h"
 
@@ -46,6 +56,10 @@ struct Params {
   unsigned short* o;
   float* lse;
   float* ws;  // split partials: O [splits][Hkv][rows][d], m, l [splits][Hkv][rows]
+  const int32_t* qrows;  // folded path: recomputed slots i*N+n, in order
+  const int32_t* src;    // folded path: resolved source branch of every slot [B1][N]
+  const int32_t* count;  // folded path: number of recomputed slots (device)
+  const int32_t* rec_pos;  // folded path: index of each recomputed slot in qrows [B1][N]
   int B1, N, L, Hq, Hkv, G;
   int rows_total, row_tiles, splits, chunk;
   float scale_log2;  // softmax scale * log2(e), applied inside the exp2
@@ -79,6 +93,40 @@ __device__ __forceinline__ TileRange tile_range(const Params& p, int j, int spli
   return tr;
 }
 
+enum Mode { kDense = 0, kCtx = 1, kBlock = 2 };
+
+__device__ __forceinline__ int rec_count(const Params& p) { return min(max(*p.count, 0), p.B1 * p.N); }
+
+// Query rows live in this launch: every row, or G per recomputed slot.
+template <int MODE>
+__device__ __forceinline__ int live_rows(const Params& p) {
+  if (MODE != kCtx) return p.rows_total;
+  return rec_count(p) * p.G;
+}
+
+// Slot (i*N + n) of query row r (r < live rows).
+template <int MODE>
+__device__ __forceinline__ int slot_of(const Params& p, int r) {
+  if (MODE != kCtx) return r / p.G;
+  return min(max(p.qrows[r / p.G], 0), p.B1 * p.N - 1);
+}
+
+// Resolved source slot of `slot`: the slot whose q/k/v it holds.
+__device__ __forceinline__ int source_slot(const Params& p, int slot) {
+  const int sb = min(max(p.src[slot], 0), p.B1 - 1);
+  return sb * p.N + slot % p.N;
+}
+
+// Row of k_blk / v_blk holding block key `key` (0-based over the branches
+// i_lo, i_lo+1, ...): the branch's own row, or on the folded path the row of
+// the slot's resolved source branch.
+template <bool FOLD>
+__device__ __forceinline__ size_t block_key_row(const Params& p, int i_lo, int key) {
+  const int slot = i_lo * p.N + key;
+  if (!FOLD) return (size_t)slot;
+  return (size_t)source_slot(p, slot);
+}
+
 // Registers holding one K/V tile between its global loads and its LDS stores.
 // K: chunk c = t + 256*i (i < D/32) is key c / (D/8), dims (c % (D/8)) * 8.
 // V: thread t < 2*D takes keys 4*(t%16) .. +4 and dims 8*(t/16) .. +8, so that
@@ -92,11 +140,32 @@ struct TileRegs {
 
 // Loads are unconditional: rows past `count` re-read the tile's last key
 // (their scores are masked to -inf and their probabilities are 0).
-template <int D>
+template <int D, bool FOLD>
 __device__ __forceinline__ void tile_load(TileRegs<D>& tr, const Params& p, const TileRange& r, int g,
                                           int i_lo) {
   const int t = threadIdx.x;
   constexpr int parts = D / 8;
+  const int last = r.count - 1;
+  if (FOLD && !r.ctx) {  // block keys through the slots' resolved sources
+    const size_t stride = (size_t)p.Hkv * D;
+    const unsigned short* kb = p.k_blk + (size_t)g * D;
+    const unsigned short* vb = p.v_blk + (size_t)g * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int c = t + kThreads * i;
+      const size_t row = block_key_row<true>(p, i_lo, r.key0 + min(c / parts, last));
+      tr.k[i] = ld16(kb + row * stride + (c % parts) * 8);
+    }
+    if (t < 2 * D) {
+      const int kg = t % 16, dg = t / 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const size_t row = block_key_row<true>(p, i_lo, r.key0 + min(kg * 4 + q, last));
+        tr.v[q] = ld16(vb + row * stride + dg * 8);
+      }
+    }
+    return;
+  }
   const unsigned short* kbase;
   const unsigned short* vbase;
   size_t stride;
@@ -109,7 +178,6 @@ __device__ __forceinline__ void tile_load(TileRegs<D>& tr, const Params& p, cons
     vbase = p.v_blk + (((size_t)i_lo * p.N + r.key0) * p.Hkv + g) * D;
     stride = (size_t)p.Hkv * D;
   }
-  const int last = r.count - 1;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     const int c = t + kThreads * i;
@@ -150,7 +218,7 @@ __device__ __forceinline__ void tile_store(Smem<D>& sm, int buf, const TileRegs<
   }
 }
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   __shared__ Smem<D> sm;
   constexpr int DS = D / 16;  // MFMA k-steps over the head dim
@@ -160,8 +228,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int lid = xcd_logical_block(blockIdx.x, total);
   const int tile = lid % p.row_tiles;
   const int gs = lid / p.row_tiles;
-  const int split = gs % p.splits;
-  const int g = gs / p.splits;
+  const int nsplit = MODE == kBlock ? 1 : p.splits;  // the block pass has no context splits
+  const int split = gs % nsplit;
+  const int g = gs / nsplit;
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -169,17 +238,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int col = lane % 32;
 
   const int row0 = tile * kRows;
+  const int rows_live = live_rows<MODE>(p);
+  if (MODE == kCtx && row0 >= rows_live) return;  // whole workgroup: no barrier reached yet
   const int rho = row0 + wave * 32 + col;  // this lane's query row
-  const bool row_ok = rho < p.rows_total;
-  const int NG = p.N * p.G;
-  const int my_branch = row_ok ? rho / NG : -1;
+  const bool row_ok = rho < rows_live;
+  const int rq = min(rho, rows_live - 1);
+  const int bn_q = slot_of<MODE>(p, rq);
+  const int my_branch = row_ok ? bn_q / p.N : -1;
 
   // Q fragment of this lane's row: dims s*16 + half*8 .. +8 for each step s
   u32x4 qf[DS];
   {
-    const int rq = min(rho, p.rows_total - 1);
-    const int bn = rq / p.G, j = rq % p.G;
-    const size_t qoff = ((size_t)bn * p.Hq + (size_t)g * p.G + j) * D;
+    const int j = rq % p.G;
+    const int qslot = MODE == kBlock ? source_slot(p, bn_q) : bn_q;
+    const size_t qoff = ((size_t)qslot * p.Hq + (size_t)g * p.G + j) * D;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = ld16(p.q + qoff + s * 16 + half * 8);
   }
@@ -190,18 +262,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   float m_run = -INFINITY;  // running max of the raw scores q.k
   float l_run = 0.f;        // running denominator (scaled to m_run), this half's keys only
 
-  const int last_row = min(row0 + kRows, p.rows_total) - 1;
-  const int i_lo = row0 / NG;
-  const int i_hi = last_row / NG;
+  const int last_row = min(row0 + kRows, rows_live) - 1;
+  const int i_lo = slot_of<MODE>(p, row0) / p.N;
+  const int i_hi = slot_of<MODE>(p, last_row) / p.N;
   const int ctx_lo = split * p.chunk;
-  const int ctx_keys = max(0, min(p.L, ctx_lo + p.chunk) - ctx_lo);
+  const int ctx_keys = MODE == kBlock ? 0 : max(0, min(p.L, ctx_lo + p.chunk) - ctx_lo);
   const int ctx_tiles = (ctx_keys + kKeys - 1) / kKeys;
-  const int blk_keys = split == p.splits - 1 ? (i_hi - i_lo + 1) * p.N : 0;
+  const int blk_keys = MODE == kCtx ? 0
+                       : (MODE == kBlock || split == p.splits - 1) ? (i_hi - i_lo + 1) * p.N : 0;
   const int ntiles = ctx_tiles + (blk_keys + kKeys - 1) / kKeys;
 
   TileRegs<D> tr;
   if (ntiles > 0) {
-    tile_load<D>(tr, p, tile_range(p, 0, split, ctx_tiles, blk_keys), g, i_lo);
+    tile_load<D, MODE == kBlock>(tr, p, tile_range(p, 0, split, ctx_tiles, blk_keys), g, i_lo);
     tile_store<D>(sm, 0, tr);
   }
   __syncthreads();
@@ -209,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     const int buf = j & 1;
     const TileRange cur = tile_range(p, j, split, ctx_tiles, blk_keys);
     const bool more = j + 1 < ntiles;
-    if (more) tile_load<D>(tr, p, tile_range(p, j + 1, split, ctx_tiles, blk_keys), g, i_lo);
+    if (more) tile_load<D, MODE == kBlock>(tr, p, tile_range(p, j + 1, split, ctx_tiles, blk_keys), g, i_lo);
 
     // S^T tile: 2 blocks of 32 keys x 32 rows
     floatx16 st[2];
@@ -305,10 +378,64 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (!row_ok) return;
+  if (MODE == kBlock) {
+    // merge the context state of the source row (kCtx partials), then write
+    const size_t orow = ((size_t)bn_q * p.Hq + (size_t)g * p.G + rho % p.G);
+    const float mb = m_run * p.scale_log2;
+    float M = mb;
+    size_t crow = 0;
+    const size_t nstate = (size_t)p.splits * p.Hkv * p.rows_total;
+    const float* mp = p.ws + nstate * D;
+    if (p.L > 0) {
+      const int ss = source_slot(p, bn_q);
+      const int cidx = min(max(p.rec_pos[ss], 0), max(rec_count(p) - 1, 0));
+      crow = (size_t)cidx * p.G + rho % p.G;
+      for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, mp[((size_t)sp * p.Hkv + g) * p.rows_total + crow]);
+    }
+    const float fb = exp2_fast(mb - M);
+    float Z = l_tot * fb;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[b][r] *= fb;
+    if (p.L > 0) {
+      for (int sp = 0; sp < p.splits; ++sp) {
+        const size_t prow = ((size_t)sp * p.Hkv + g) * p.rows_total + crow;
+        const float w = mp[nstate + prow] * exp2_fast(mp[prow] - M);
+        Z += w;
+        const float* op = p.ws + prow * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 v = *(const float4*)(op + b * 32 + 8 * q4 + 4 * half);
+            acc[b][4 * q4 + 0] = fmaf(w, v.x, acc[b][4 * q4 + 0]);
+            acc[b][4 * q4 + 1] = fmaf(w, v.y, acc[b][4 * q4 + 1]);
+            acc[b][4 * q4 + 2] = fmaf(w, v.z, acc[b][4 * q4 + 2]);
+            acc[b][4 * q4 + 3] = fmaf(w, v.w, acc[b][4 * q4 + 3]);
+          }
+        }
+      }
+    }
+    const float inv = 1.f / Z;
+    unsigned short* out = p.o + orow * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dcol = b * 32 + 8 * q4 + 4 * half;
+        uint2 w;
+        w.x = pack_bf16x2(acc[b][4 * q4 + 0] * inv, acc[b][4 * q4 + 1] * inv);
+        w.y = pack_bf16x2(acc[b][4 * q4 + 2] * inv, acc[b][4 * q4 + 3] * inv);
+        *(uint2*)(out + dcol) = w;
+      }
+    }
+    if (half == 0) p.lse[orow] = (M + log2f(Z)) * 0.69314718055994531f;
+    return;
+  }
   const float inv_l = 1.f / l_tot;
-  if (p.splits == 1) {
-    const int bn = rho / p.G, j = rho % p.G;
-    const size_t orow = ((size_t)bn * p.Hq + (size_t)g * p.G + j);
+  if (MODE == kDense && p.splits == 1) {
+    const size_t orow = ((size_t)bn_q * p.Hq + (size_t)g * p.G + rho % p.G);
     unsigned short* out = p.o + orow * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -384,11 +511,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(Params p) {
 template <int D>
 hipError_t launch_d(const Params& p, hipStream_t stream) {
   const int blocks = p.row_tiles * p.Hkv * p.splits;
-  hipLaunchKernelGGL(attn_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<D, kDense>), dim3(blocks), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const size_t items = (size_t)p.Hkv * p.rows_total * (D / 4);
-  hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Folded: context states of the recomputed rows, then every row's block keys
+// merged with its source row's context state.
+template <int D>
+hipError_t launch_folded_d(const Params& p, hipStream_t stream) {
+  if (p.L > 0) {
+    hipLaunchKernelGGL((attn_kernel<D, kCtx>), dim3(p.row_tiles * p.Hkv * p.splits), dim3(kThreads), 0, stream,
+                       p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((attn_kernel<D, kBlock>), dim3(p.row_tiles * p.Hkv), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -414,14 +555,21 @@ AttnPlan attn_plan(int B1, int N, int L, int Hq, int Hkv, int d) {
   pl.splits = splits;
   pl.chunk = chunk;
   pl.ws_bytes = splits > 1 ? (size_t)splits * Hkv * pl.rows_total * (d + 2) * sizeof(float) : 0;
+  pl.ws_bytes_folded = L > 0 ? (size_t)splits * Hkv * pl.rows_total * (d + 2) * sizeof(float) : 0;
   return pl;
 }
 
 hipError_t launch_attention(const void* q, const void* k_blk, const void* v_blk,
                             const void* k_ctx, const void* v_ctx, int B1, int N, int L,
                             int Hq, int Hkv, int d, float scale, void* o, float* lse,
-                            void* ws, const AttnPlan& plan, hipStream_t stream) {
+                            void* ws, const AttnPlan& plan, hipStream_t stream,
+                            const int32_t* rec_rows, const int32_t* src, const int32_t* rec_count,
+                            const int32_t* rec_pos) {
   Params p;
+  p.qrows = rec_rows;
+  p.src = src;
+  p.count = rec_count;
+  p.rec_pos = rec_pos;
   p.q = (const unsigned short*)q;
   p.k_blk = (const unsigned short*)k_blk;
   p.v_blk = (const unsigned short*)v_blk;
@@ -441,10 +589,11 @@ hipError_t launch_attention(const void* q, const void* k_blk, const void* v_blk,
   p.splits = plan.splits;
   p.chunk = plan.chunk;
   p.scale_log2 = scale * 1.4426950408889634f;
+  const bool fold = rec_rows != nullptr;
   switch (d) {
-    case 32: return launch_d<32>(p, stream);
-    case 64: return launch_d<64>(p, stream);
-    case 128: return launch_d<128>(p, stream);
+    case 32: return fold ? launch_folded_d<32>(p, stream) : launch_d<32>(p, stream);
+    case 64: return fold ? launch_folded_d<64>(p, stream) : launch_d<64>(p, stream);
+    case 128: return fold ? launch_folded_d<128>(p, stream) : launch_d<128>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -13,14 +13,22 @@ struct AttnPlan {
   int splits;      // context key ranges
   int chunk;       // context keys per range (multiple of 64)
   size_t ws_bytes;
+  size_t ws_bytes_folded;  // folded path: context states of every row slot
 };
 
 AttnPlan attn_plan(int B1, int N, int L, int Hq, int Hkv, int d);
 
+// With rec_rows non-null (folded verification): the context is attended by
+// the rec_count[0] slots listed in rec_rows only, and every slot attends its
+// branch's block keys (read through src) with its source's query, merged
+// with its source row's context state (rec_pos maps a slot to its index in
+// rec_rows).  The workspace is then plan.ws_bytes_folded.
 hipError_t launch_attention(const void* q, const void* k_blk, const void* v_blk,
                             const void* k_ctx, const void* v_ctx, int B1, int N, int L,
                             int Hq, int Hkv, int d, float scale, void* o, float* lse,
-                            void* ws, const AttnPlan& plan, hipStream_t stream);
+                            void* ws, const AttnPlan& plan, hipStream_t stream,
+                            const int32_t* rec_rows = nullptr, const int32_t* src = nullptr,
+                            const int32_t* rec_count = nullptr, const int32_t* rec_pos = nullptr);
 
 hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows,
                               int32_t* count, hipStream_t stream);
@@ -64,5 +72,11 @@ hipError_t launch_match(const int32_t* state, const int32_t* next_state, const i
                         int32_t* n_accepted, int32_t* status, hipStream_t stream);
 
 hipError_t launch_selfcheck(double* out, hipStream_t stream);
+
+hipError_t launch_fold_gate(const void* H, const TreeArgs& tree, int N, int D, float delta,
+                            int32_t* recompute, int32_t* src, int32_t* rec_rows, int32_t* rec_count,
+                            int32_t* rec_pos, int32_t* branch_off, hipStream_t stream);
+
+
 
 }  // namespace sfv

@@ -22,7 +22,8 @@ SFV_MASK = -1
 EXPORTS = [
     "sfv_last_error", "sfv_version", "sfv_attend_workspace_bytes", "sfv_attend_branches",
     "sfv_masked_rows", "sfv_lm_head", "sfv_commit_workspace_bytes", "sfv_commit",
-    "sfv_match_tree", "sfv_selfcheck_bounds",
+    "sfv_match_tree", "sfv_selfcheck_bounds", "sfv_fold_gate", "sfv_attend_folded_workspace_bytes",
+    "sfv_attend_folded",
 ]
 
 _lib = None
@@ -63,6 +64,9 @@ def load(path: str = LIB_PATH):
     lib.sfv_commit.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P, SZ, P]
     lib.sfv_match_tree.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
     lib.sfv_selfcheck_bounds.argtypes = [P, P]
+    lib.sfv_fold_gate.argtypes = [P, P, I, I, I, F, P, P, P, P, P, P, P]
+    lib.sfv_attend_folded_workspace_bytes.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
+    lib.sfv_attend_folded.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, P, P, P, P, SZ, P]
     for name in EXPORTS:
         if name not in ("sfv_last_error", "sfv_version"):
             getattr(lib, name).restype = I
@@ -152,3 +156,26 @@ def sfv_match_tree(state, next_state, commit_pos, parent_host, B1, N, k_max, S_m
 
 def sfv_selfcheck_bounds(out, stream=None):
     return _check(load().sfv_selfcheck_bounds(_ptr(out), _stream(stream)))
+
+
+def sfv_fold_gate(hidden, parent_host, B1, N, D, delta, recompute, src, rec_rows, rec_count,
+                  rec_pos, branch_off, stream=None):
+    par = _host_i32(parent_host)
+    return _check(load().sfv_fold_gate(
+        _ptr(hidden), ctypes.cast(par, ctypes.c_void_p), B1, N, D, float(delta), _ptr(recompute),
+        _ptr(src), _ptr(rec_rows), _ptr(rec_count), _ptr(rec_pos), _ptr(branch_off), _stream(stream)))
+
+
+def sfv_attend_folded_workspace_bytes(B1, N, L, Hq, Hkv, d) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().sfv_attend_folded_workspace_bytes(B1, N, L, Hq, Hkv, d, ctypes.byref(out)))
+    return out.value
+
+
+def sfv_attend_folded(q, k_blk, v_blk, k_ctx, v_ctx, B1, N, L, Hq, Hkv, d, softmax_scale, src,
+                      rec_rows, rec_count, rec_pos, o, lse, workspace=None, workspace_bytes=0,
+                      stream=None):
+    return _check(load().sfv_attend_folded(
+        _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx), B1, N, L, Hq, Hkv, d,
+        float(softmax_scale), _ptr(src), _ptr(rec_rows), _ptr(rec_count), _ptr(rec_pos), _ptr(o),
+        _ptr(lse), _ptr(workspace), int(workspace_bytes), _stream(stream)))

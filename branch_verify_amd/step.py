@@ -150,3 +150,54 @@ def step_for(wl, inp: dict, device="cuda", S_max=None, k_max=1, tau=0.0) -> Veri
     return VerifyStep(wl.B1, wl.N, wl.L, wl.Hq, wl.Hkv, wl.d, wl.D, wl.V, M, inp["parent"], wl.T,
                       wl.seed, wl.step0, wl.pos0, S_max=wl.S_t if S_max is None else S_max,
                       k_max=k_max, tau=tau, device=device)
+
+
+class FoldedAttention:
+    """SpecFold folded verification of the attention rows of one branch batch:
+    the parent-child gate on the layer-input hidden states, then attention
+    with recomputed rows computed and folded rows corrected from their source.
+    Buffers are allocated once per shape; both calls are stream-ordered."""
+
+    def __init__(self, B1, N, L, Hq, Hkv, d, D, parent, device="cuda"):
+        sfv.load()
+        self.B1, self.N, self.L, self.Hq, self.Hkv, self.d, self.D = B1, N, L, Hq, Hkv, d, D
+        self.parent = [int(x) for x in parent]
+        self.scale = 1.0 / math.sqrt(d)
+        dev = device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.recompute = torch.empty((B1, N), **i32)
+        self.src = torch.empty((B1, N), **i32)
+        self.rec_rows = torch.empty(B1 * N, **i32)
+        self.rec_count = torch.empty(1, **i32)
+        self.rec_pos = torch.empty((B1, N), **i32)
+        self.branch_off = torch.empty(B1 + 1, **i32)
+        self.o = torch.empty((B1, N, Hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B1, N, Hq), dtype=torch.float32, device=dev)
+        self.ws_bytes = sfv.sfv_attend_folded_workspace_bytes(B1, N, L, Hq, Hkv, d)
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+
+    def gate(self, h_layer, delta, stream=None):
+        sfv.sfv_fold_gate(h_layer, self.parent, self.B1, self.N, self.D, delta, self.recompute,
+                          self.src, self.rec_rows, self.rec_count, self.rec_pos, self.branch_off,
+                          stream)
+
+    def attend(self, x, stream=None):
+        sfv.sfv_attend_folded(x["q"], x["k_blk"], x["v_blk"], x["k_ctx"], x["v_ctx"], self.B1,
+                              self.N, self.L, self.Hq, self.Hkv, self.d, self.scale, self.src,
+                              self.rec_rows, self.rec_count, self.rec_pos, self.o, self.lse,
+                              self.ws, self.ws_bytes, stream)
+
+    def run(self, x, h_layer, delta, stream=None):
+        self.gate(h_layer, delta, stream)
+        self.attend(x, stream)
+
+    def lists(self) -> dict:
+        torch.cuda.synchronize()
+        cnt = int(self.rec_count.item())
+        return dict(recompute=self.recompute.cpu().numpy().astype(bool), src=self.src.cpu().numpy(),
+                    rec_rows=self.rec_rows[:cnt].cpu().numpy(), count=cnt,
+                    rec_pos=self.rec_pos.cpu().numpy(), branch_off=self.branch_off.cpu().numpy())
+
+
+def folded_for(wl, parent, device="cuda") -> FoldedAttention:
+    return FoldedAttention(wl.B1, wl.N, wl.L, wl.Hq, wl.Hkv, wl.d, wl.D, parent, device=device)

@@ -86,6 +86,64 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Fold gate for folded verification.  SpecFold, Sec. 3.2 (Eq. 4-5: the
+ * per-token parent-child relative residual of the layer-input hidden state,
+ * fold iff rho <= delta) and App. B (the main branch recomputes everything;
+ * sources resolved to the nearest recomputed ancestor; compacted lists).
+ *
+ * For draft i >= 1 with parent p and position n:
+ *   num = ||H_i[n] - H_p[n]||^2, den = ||H_p[n]||^2 (fp64 sums of the bf16
+ *   values); recompute[i][n] = !(delta >= 0 && num <= delta^2 * den), with
+ *   delta^2 formed in fp64 from the fp32 argument.  recompute[0][n] = 1.
+ *   src[i][n] = i if recompute[i][n], else src[p][n] (nearest recomputed
+ *   ancestor; the slot's Q/K/V are that branch's).
+ *   rec_rows: flat i*N + n of every recomputed slot, in increasing order;
+ *   rec_count[0] = their number; rec_pos[i][n] = the slot's index in
+ *   rec_rows, -1 when folded; branch i's entries are
+ *   rec_rows[branch_off[i] .. branch_off[i+1]).
+ *
+ *   hidden [B1][N][D] bf16, 16-byte aligned; parent_host as for sfv_commit
+ *   recompute, src, rec_pos [B1][N] int32 out; rec_rows [B1*N] int32 out
+ *   rec_count [1] int32 out; branch_off [B1+1] int32 out
+ * Supported: D % 8 == 0; 1 <= B1 <= 64; 1 <= N <= 256; delta not NaN
+ * (a negative delta folds nothing).  Two kernels on `stream`, no workspace.
+ */
+int sfv_fold_gate(const void* hidden, const int32_t* parent_host, int B1, int N, int D, float delta,
+                  int32_t* recompute, int32_t* src, int32_t* rec_rows, int32_t* rec_count,
+                  int32_t* rec_pos, int32_t* branch_off, void* stream);
+
+/*
+ * Folded-verification attention.  SpecFold, Sec. 3.2 and App. A.1 (a folded
+ * position inherits its parent's query, key and value, and its attention
+ * output stays exact with respect to its branch's own K/V table) and App. B
+ * (only recomputed rows stream the shared prefix; folded rows reuse their
+ * source row's streaming-softmax state).
+ *
+ * With the tables resolved by src (slot (i, n) holds the q/k/v of branch
+ * src[i][n] at n), every (i, n, h) gets the output sfv_attend_branches would
+ * give for the resolved q over [context | branch i's resolved block keys].
+ * The recomputed slots (rec_rows, rec_count) attend the context; every slot
+ * then attends its branch's resolved block keys with its resolved query and
+ * merges in the context state (m, Z, O) of its source row (rec_pos).  A
+ * folded slot's query and the context are its source's, so that state is
+ * its own: folded rows never read the context and nothing is subtracted.
+ * q/k/v at folded slots are never read.
+ *
+ *   Shapes and dtypes as sfv_attend_branches; src, rec_rows, rec_count,
+ *   rec_pos as written by sfv_fold_gate.  Other index values give
+ *   unspecified outputs but never an out-of-bounds access.
+ *   workspace: sfv_attend_folded_workspace_bytes (0 when L = 0) bytes, holding
+ *   the context states of the recomputed rows.
+ */
+int sfv_attend_folded_workspace_bytes(int B1, int N, int L, int Hq, int Hkv, int d, size_t* bytes);
+int sfv_attend_folded(const void* q, const void* k_blk, const void* v_blk,
+                      const void* k_ctx, const void* v_ctx,
+                      int B1, int N, int L, int Hq, int Hkv, int d, float softmax_scale,
+                      const int32_t* src, const int32_t* rec_rows, const int32_t* rec_count,
+                      const int32_t* rec_pos, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Masked-row list.  SpecFold, introduction: the forward map returns token
  * distributions for the masked positions of the active block.
  *   state [B1][N] int32 (SFV_MASK = masked)

@@ -145,3 +145,48 @@ def test_single_hip_runtime_in_process(lib):
     maps = open("/proc/self/maps").read()
     libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(libs) <= 1, libs
+
+
+def test_fold_gate_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    par = (ctypes.c_int32 * 3)(-1, 0, 1)
+    pp = ctypes.cast(par, P)
+    F = ctypes.c_float
+
+    def call(h=f, tree=pp, N=8, D=64, delta=0.1, last=f):
+        return lib.sfv_fold_gate(h, tree, 3, N, D, F(delta), f, f, f, f, f, last, None)
+
+    assert call(last=None) == sfv.SFV_E_INVAL
+    assert call(D=60) == sfv.SFV_E_UNSUPPORTED
+    assert call(delta=float("nan")) == sfv.SFV_E_INVAL
+    assert call(h=P(0x1008)) == sfv.SFV_E_INVAL
+    assert call(N=0) == sfv.SFV_E_INVAL
+    bad = (ctypes.c_int32 * 3)(-1, 2, 0)
+    assert call(tree=ctypes.cast(bad, P)) == sfv.SFV_E_TREE
+
+
+def test_attend_folded_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    F = ctypes.c_float
+
+    def call(q=f, B1=3, G=(4, 2), d=32, scale=0.17, src=f, ws=1 << 30, o=f, N=8, rec_pos=f):
+        return lib.sfv_attend_folded(q, f, f, f, f, B1, N, 64, G[0], G[1], d, F(scale), src, f, f,
+                                     rec_pos, o, f, f, ws, None)
+
+    assert call(q=None) == sfv.SFV_E_INVAL
+    assert call(src=None) == sfv.SFV_E_INVAL
+    assert call(rec_pos=None) == sfv.SFV_E_INVAL
+    assert call(d=96) == sfv.SFV_E_UNSUPPORTED
+    assert call(G=(48, 3)) == sfv.SFV_E_UNSUPPORTED
+    assert call(scale=float("nan")) == sfv.SFV_E_INVAL
+    assert call(o=P(0x1002)) == sfv.SFV_E_INVAL
+    assert call(B1=0) == sfv.SFV_E_INVAL
+    assert call(N=257) == sfv.SFV_E_INVAL
+    rc, need = _ws(lib.sfv_attend_folded_workspace_bytes, 3, 8, 64, 4, 2, 32)
+    assert rc == sfv.SFV_OK and need > 0          # context states even with one split
+    assert call(ws=need - 1) == sfv.SFV_E_WORKSPACE
+    rc, need0 = _ws(lib.sfv_attend_folded_workspace_bytes, 3, 8, 0, 4, 2, 32)
+    assert rc == sfv.SFV_OK and need0 == 0        # no context, no workspace
+    assert _ws(lib.sfv_attend_folded_workspace_bytes, 3, 8, 64, 4, 2, 96)[0] == sfv.SFV_E_UNSUPPORTED
