@@ -22,6 +22,7 @@ Recipe (every tensor has its own numpy stream, so any subset can be drawn):
   streams [seed, 10..15]  q, k_blk, v_blk, k_ctx, v_ctx, hidden   N(0, 1)
   streams [seed, 16, c]   W rows in chunks of 4096                N(0, w_std)
   streams [seed, 17, 18]  layer-input hidden states of the fold gate (below)
+  stream [seed, 19, c]    stand-in fp32 logits for the commit (draw_logits)
 All floats are drawn in fp32 and rounded to bfloat16 (round to nearest even).
 
 Layer-input hidden states for SpecFold's parent-child gate (Sec. 3.1
@@ -238,6 +239,19 @@ def draw_fold_hidden(wl: Workload, parent: np.ndarray, state: np.ndarray,
         H[i] = H[p] + sig[:, None] * rz.standard_normal((N, D), dtype=np.float32)
         H[i] = bf16_bits_to_f32(f32_to_bf16_bits(H[i]))
     return f32_to_bf16_bits(H)
+
+
+def draw_logits(M: int, V: int, seed: int, chunk: int = 64) -> np.ndarray:
+    """fp32 [M][V] stand-in logits for testing the commit on its own: N(0, 1)
+    rows scaled by a per-row sharpness s ~ LogU(0.5, 8), so the row
+    confidences range from near-uniform to peaked."""
+    out = np.empty((M, V), dtype=np.float32)
+    for c0 in range(0, M, chunk):
+        rng = _rng(seed, 19, c0 // chunk)
+        rows = min(chunk, M - c0)
+        sharp = np.exp(rng.uniform(np.log(0.5), np.log(8.0), (rows, 1))).astype(np.float32)
+        out[c0:c0 + rows] = rng.standard_normal((rows, V), dtype=np.float32) * sharp
+    return out
 
 
 def masked_count(state: np.ndarray) -> int:

@@ -2,7 +2,9 @@
 
 Acceptance (same seeded inputs on both sides):
   * commit and match: tokens, committed positions, next states and matched
-    draft indices bit-exact given the same fp32 logits;
+    draft indices bit-exact given the same seeded fp32 logits (drawn on the
+    host, fed to both); on the LM head's own logits the commit is checked by
+    properties (first argmax, confidence, argmax position, next state, walk);
   * attention: O within 2e-2 max-abs (bf16 in, fp32 accumulation), LSE within
     1e-5 relative;
   * LM-head logits within 3e-2 max-abs.
@@ -85,7 +87,8 @@ def check_attention(x, step, full):
 # LM head
 # ---------------------------------------------------------------------------
 def check_lm_head(x, res, full):
-    rows = res["rows"]
+    rows = O.masked_rows(x["state"])
+    assert np.array_equal(res["rows"], rows)
     logits = res["logits"]
     M, V = logits.shape
     hidden = f32(x["hidden"])
@@ -110,9 +113,10 @@ def check_lm_head(x, res, full):
 # ---------------------------------------------------------------------------
 # commit and match
 # ---------------------------------------------------------------------------
-def check_commit_match(x, res, wl_T, seed, step0, pos0, S_max, logits_host=None, k_max=1, tau=0.0):
-    rows = res["rows"]
-    lg = res["logits"].cpu().numpy() if logits_host is None else logits_host
+def check_commit_match(x, res, wl_T, seed, step0, pos0, S_max, logits_host, k_max=1, tau=0.0):
+    rows = O.masked_rows(x["state"])
+    assert np.array_equal(res["rows"], rows)
+    lg = logits_host
     nxt, cpos, tok, conf, S = O.commit(lg, rows, x["state"], x["parent"], wl_T, seed, step0, pos0,
                                        k_max=k_max, tau=tau)
     assert np.array_equal(res["token"], tok), np.flatnonzero(res["token"] != tok)[:10]
@@ -127,6 +131,57 @@ def check_commit_match(x, res, wl_T, seed, step0, pos0, S_max, logits_host=None,
     assert res["h"] == h
     assert np.array_equal(res["chain"], chain)
     return h
+
+
+def commit_on(step, xd, lg_host):
+    """Commit and walk of `step` on host logits; returns results like step.results()."""
+    lg = torch.from_numpy(lg_host).cuda()
+    step.commit(xd, logits=lg)
+    step.match(xd)
+    torch.cuda.synchronize()
+    res = step.results()
+    del lg
+    return res
+
+
+def check_commit_properties(x, res, wl):
+    """The commit on the LM head's own logits, by properties of its outputs:
+    conf = 1/sum exp(l - max) (fp64 on the device); at T = 0 each token is the
+    row's first argmax; each branch commits a masked position of maximal
+    confidence (up to the fast path's relative bound) and nothing else; the
+    walk follows equal states from the main branch."""
+    lg = res["logits"]
+    rows = res["rows"]
+    M = rows.size
+    state, parent = x["state"], x["parent"]
+    B1, N = state.shape
+    conf = res["conf"].astype(np.float64)
+    if M:
+        l64 = lg.double()
+        S = torch.exp(l64 - l64.max(dim=1, keepdim=True).values).sum(dim=1).cpu().numpy()
+        assert np.max(np.abs(conf * S - 1.0)) <= 1e-5
+        if wl.T == 0.0:
+            assert np.array_equal(res["token"], torch.argmax(lg, dim=1).int().cpu().numpy())
+    where = {int(r): k for k, r in enumerate(rows)}
+    nxt, cpos = res["next_state"], res["commit_pos"][:, 0]
+    for i in range(B1):
+        masked = [n for n in range(N) if state[i, n] == O.MASK]
+        if not masked:
+            assert cpos[i] == -1 and np.array_equal(nxt[i], state[i])
+            continue
+        best = max(conf[where[i * N + n]] for n in masked)
+        n = int(cpos[i])
+        assert n in masked and conf[where[i * N + n]] >= best * (1 - 3e-5)
+        want = state[i].copy()
+        want[n] = res["token"][where[i * N + n]]
+        assert np.array_equal(nxt[i], want)
+    cur, h = 0, res["h"]
+    for k in range(h):
+        j = int(res["chain"][k])
+        hits = [b for b in range(1, B1) if np.array_equal(state[b], nxt[cur])]
+        assert hits and j == hits[0]
+        cur = j
+    say(f"commit properties hold on the LM head's logits (M={M}, h={h})")
 
 
 def run_twice(step, xd):
@@ -162,7 +217,12 @@ def test_full_step_parity(gpu_lib, idx):
     assert np.array_equal(res["rows"], O.masked_rows(x["state"]))
     check_attention(x, step, full=idx <= 4)
     check_lm_head(x, res, full=idx == 1)
-    check_commit_match(x, res, wl.T, wl.seed, wl.step0, wl.pos0, wl.S_t)
+    check_commit_properties(x, res, wl)
+    # the commit and the walk at this shape on seeded host logits, against the oracle
+    lg = synth.draw_logits(step.M, wl.V, wl.seed)
+    say(f"workload {idx}: commit + match on seeded logits")
+    res2 = commit_on(step, xd, lg)
+    check_commit_match(x, res2, wl.T, wl.seed, wl.step0, wl.pos0, wl.S_t, logits_host=lg)
     del xd, step
     torch.cuda.empty_cache()
 
@@ -509,24 +569,20 @@ def test_threshold_planted_chain(gpu_lib, case):
 
 @pytest.mark.parametrize("idx", [2, 3])
 def test_threshold_commit_workload(gpu_lib, idx):
-    """Threshold commit on the LM head's own logits at the full workload shape."""
+    """Threshold commit at the full workload shape on seeded host logits."""
     wl = synth.WORKLOADS[idx]
     x = host_inputs(idx)
     xd = to_device(x)
     step = step_for(wl, x, k_max=4, tau=0.0)
-    step.run(xd)
-    torch.cuda.synchronize()
-    res = step.results()
-    lg = res["logits"].cpu().numpy()
-    *_, conf, _S = O.commit(lg, res["rows"], x["state"], x["parent"], wl.T, wl.seed, wl.step0, wl.pos0)
+    step.masked_rows(xd)
+    lg = synth.draw_logits(step.M, wl.V, wl.seed + 1000)
+    rows = O.masked_rows(x["state"])
+    *_, conf, _S = O.commit(lg, rows, x["state"], x["parent"], wl.T, wl.seed, wl.step0, wl.pos0)
     for q in (0.0, 0.5, 0.9):
         tau = float(np.quantile(conf, q))
         step.tau = tau
         say(f"workload {idx} threshold commit k_max=4 tau={tau:.4g}")
-        step.commit(xd)
-        step.match(xd)
-        torch.cuda.synchronize()
-        res = step.results()
+        res = commit_on(step, xd, lg)
         check_commit_match(x, res, wl.T, wl.seed, wl.step0, wl.pos0, wl.S_t, logits_host=lg,
                            k_max=4, tau=tau)
     del xd, step
