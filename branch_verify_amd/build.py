@@ -25,6 +25,7 @@ SOURCES = {
     "commit.hip": ["-ffp-contract=off"],
     "match.hip": [],
     "fold.hip": ["-ffp-contract=off"],
+    "draft.hip": ["-ffp-contract=off"],
 }
 
 COMMON = [

@@ -134,6 +134,36 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk, con
                     "sfv_attend_branches");
 }
 
+int sfv_stale_topk(const float* logits, const int32_t* rows, const float* conf, int M, int V, int N,
+                   int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos, void* stream) {
+  if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
+  if (M < 0 || M > SFV_MAX_BRANCHES * N) return fail(SFV_E_INVAL, "M=%d out of range", M);
+  if (V < 1) return fail(SFV_E_INVAL, "V=%d < 1", V);
+  if (K < 1 || K > SFV_MAX_TOPK || K > V) return fail(SFV_E_INVAL, "K=%d not in [1, min(%d, V)]", K, SFV_MAX_TOPK);
+  if (branch < 0 || branch >= SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "branch=%d out of range", branch);
+  if ((double)M * V >= 9.0e15) return fail(SFV_E_INVAL, "too large");
+  if (M > 0 && (!logits || !rows || !conf || !top_ids || !top_logit || !conf_pos))
+    return fail(SFV_E_INVAL, "null pointer");
+  return hip_status(sfv::launch_stale_topk(logits, rows, conf, M, V, N, branch, K, top_ids, top_logit, conf_pos,
+                                           (hipStream_t)stream),
+                    "sfv_stale_topk");
+}
+
+int sfv_draft_tree(const int32_t* root, const int32_t* top_ids, const float* top_logit, const float* conf,
+                   int N, int K, int D, int W, float temperature, uint64_t seed, uint64_t step0, int64_t pos0,
+                   int32_t* parent, int32_t* states, int32_t* n_drafts, void* stream) {
+  if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
+  if (K < 1 || K > SFV_MAX_TOPK) return fail(SFV_E_INVAL, "K=%d not in [1, %d]", K, SFV_MAX_TOPK);
+  if (D < 0 || D > SFV_MAX_BRANCHES - 1) return fail(SFV_E_INVAL, "D=%d not in [0, %d]", D, SFV_MAX_BRANCHES - 1);
+  if (W < 0 || W > SFV_MAX_DRAFT_WIDTH) return fail(SFV_E_INVAL, "W=%d not in [0, %d]", W, SFV_MAX_DRAFT_WIDTH);
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(SFV_E_INVAL, "temperature must be >= 0");
+  if (!root || !top_ids || !top_logit || !conf || !parent || !states || !n_drafts)
+    return fail(SFV_E_INVAL, "null pointer");
+  return hip_status(sfv::launch_draft_tree(root, top_ids, top_logit, conf, N, K, D, W, temperature, seed, step0,
+                                           pos0, parent, states, n_drafts, (hipStream_t)stream),
+                    "sfv_draft_tree");
+}
+
 int sfv_fold_gate(const void* hidden, const int32_t* parent_host, int B1, int N, int D, float delta,
                   int32_t* recompute, int32_t* src, int32_t* rec_rows, int32_t* rec_count,
                   int32_t* rec_pos, int32_t* branch_off, void* stream) {

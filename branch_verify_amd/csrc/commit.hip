@@ -23,6 +23,7 @@
 // This translation unit is compiled with -ffp-contract=off.
 #include "common.h"
 #include "internal.h"
+#include "noise.h"
 
 namespace sfv {
 namespace {
@@ -89,41 +90,6 @@ size_t ws_bytes(int B1, int N, int M, int items_max, int splits) {
   return off + sizeof(Partial) * (size_t)M * splits;
 }
 
-// ---------------------------------------------------------------------------
-// Philox4x64-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
-// SC'11) and the Gumbel transform.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += W0;
-      k1 += W1;
-    }
-    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
-    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
-  }
-}
-
-// The 8 noise words of ids 8*blk .. 8*blk+7: word j = half (j & 1) of output (j >> 1).
-__device__ __forceinline__ void noise_block(uint64_t seed, uint64_t step, uint64_t pos, uint64_t blk,
-                                            unsigned w[8]) {
-  uint64_t c[4] = {blk, pos, step, 0};
-  philox4x64_10(c, seed, 0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    w[2 * j] = (unsigned)(c[j] & 0xFFFFFFFFull);
-    w[2 * j + 1] = (unsigned)(c[j] >> 32);
-  }
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -143,17 +109,6 @@ __device__ __forceinline__ float gumbel_fast(unsigned w) {
     }
   }
   return -fast_log2(L1) * ln2;
-}
-
-// The defined value: fl32(-ln(-ln u)) with both logarithms in fp64.
-__device__ __forceinline__ float gumbel_exact(unsigned w) {
-  const double u = ((double)w + 0.5) * 2.3283064365386962890625e-10;
-  return (float)(-log(-log(u)));
-}
-
-__device__ __forceinline__ double gumbel_exact_f64(unsigned w) {
-  const double u = ((double)w + 0.5) * 2.3283064365386962890625e-10;
-  return -log(-log(u));
 }
 
 // Lexicographic "better" for (value, index): larger value, then lower index.

@@ -73,6 +73,15 @@ hipError_t launch_match(const int32_t* state, const int32_t* next_state, const i
 
 hipError_t launch_selfcheck(double* out, hipStream_t stream);
 
+hipError_t launch_stale_topk(const float* logits, const int32_t* rows, const float* conf, int M, int V, int N,
+                             int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos,
+                             hipStream_t stream);
+
+hipError_t launch_draft_tree(const int32_t* root, const int32_t* top_ids, const float* top_logit,
+                             const float* conf, int N, int K, int D, int W, float temperature, uint64_t seed,
+                             uint64_t step0, int64_t pos0, int32_t* parent, int32_t* states, int32_t* n_drafts,
+                             hipStream_t stream);
+
 hipError_t launch_fold_gate(const void* H, const TreeArgs& tree, int N, int D, float delta,
                             int32_t* recompute, int32_t* src, int32_t* rec_rows, int32_t* rec_count,
                             int32_t* rec_pos, int32_t* branch_off, hipStream_t stream);

@@ -51,6 +51,8 @@ enum {
 #define SFV_MASK (-1)
 #define SFV_MAX_BRANCHES 64  /* B1 limit: the tree is host control data */
 #define SFV_MAX_BLOCK 256    /* N limit */
+#define SFV_MAX_TOPK 32      /* stale conditionals per position */
+#define SFV_MAX_DRAFT_WIDTH 16  /* children offered per draft-tree node */
 
 /* Message of the last non-OK return on this thread ("" if none). */
 const char* sfv_last_error(void);
@@ -84,6 +86,49 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk,
                         int B1, int N, int L, int Hq, int Hkv, int d, float softmax_scale,
                         void* o, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stale conditionals for drafting.  SPOT, "How does SPOT draft and verify?"
+ * (the drafter reads the target's latest top-32 probabilities at each masked
+ * position) and "Important context" (stale conditionals).
+ *
+ * For every masked row r (rows as from sfv_masked_rows) of branch `branch`,
+ * n = rows[r] % N: top_ids[n][0..K) = the K vocab ids with the largest
+ * logits[r][.], by value, ties to the lower id; top_logit[n][k] their fp32
+ * logits; conf_pos[n] = conf[r] (as sfv_commit wrote it).  Entries of
+ * positions with no row are left untouched.
+ *   logits [M][V] fp32; rows [M] int32; conf [M] fp32
+ *   top_ids [N][K] int32 out; top_logit [N][K] fp32 out; conf_pos [N] fp32 out
+ * Supported: 1 <= K <= min(32, V).  One workgroup per row (two passes over it).
+ */
+int sfv_stale_topk(const float* logits, const int32_t* rows, const float* conf, int M, int V, int N,
+                   int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos, void* stream);
+
+/*
+ * Draft tree from stale conditionals.  SPOT, "Important context" (block
+ * states grown by predicting the next committed position, high-probability
+ * branches first, up to D drafted states; coupled-noise match) and "How does
+ * SPOT differ from Spiffy, SSD and BlockSpec?" (SSD-style confidence chain,
+ * BlockSpec-style confidence tree).
+ *
+ * From root [N] (SFV_MASK = masked) with, per masked position n, its top-K
+ * ids/logits and confidence c_n: a node u offers its W most confident masked
+ * positions (c descending, ties to the lower position) as children; child
+ * u+n has probability P(u) * c_n / sum_{m masked in u} c_m (fp64, the sum in
+ * increasing m); nodes are added best-first (probability, then lower parent
+ * index, then lower position) until D drafts.  W = 0 or 1 gives the chain.
+ * Drafted token at n from a node of depth d: T = 0, top_ids[n][0]; T > 0, the
+ * id maximising fl32(fl32(l * fl32(1/T)) + g(seed, step0 + d, pos0 + n, id))
+ * over the K candidates (the commit's noise), ties to the lower id.
+ *   parent [D+1] int32 out (parent[0] = -1); states [D+1][N] int32 out
+ *   n_drafts [1] int32 out: drafts built; branches past it copy the root
+ *   (parent 0).
+ * Supported: 0 <= D <= 63, 0 <= W <= 16, 1 <= K <= 32, T >= 0 finite.
+ * One workgroup; no workspace.
+ */
+int sfv_draft_tree(const int32_t* root, const int32_t* top_ids, const float* top_logit, const float* conf,
+                   int N, int K, int D, int W, float temperature, uint64_t seed, uint64_t step0, int64_t pos0,
+                   int32_t* parent, int32_t* states, int32_t* n_drafts, void* stream);
 
 /*
  * Fold gate for folded verification.  SpecFold, Sec. 3.2 (Eq. 4-5: the

@@ -190,3 +190,38 @@ def test_attend_folded_validation(lib):
     rc, need0 = _ws(lib.sfv_attend_folded_workspace_bytes, 3, 8, 0, 4, 2, 32)
     assert rc == sfv.SFV_OK and need0 == 0        # no context, no workspace
     assert _ws(lib.sfv_attend_folded_workspace_bytes, 3, 8, 64, 4, 2, 96)[0] == sfv.SFV_E_UNSUPPORTED
+
+
+def test_stale_topk_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+
+    def call(M=4, V=512, N=8, branch=0, K=32, ptr=f):
+        return lib.sfv_stale_topk(ptr, f, f, M, V, N, branch, K, f, f, f, None)
+
+    assert call(K=0) == sfv.SFV_E_INVAL
+    assert call(K=33) == sfv.SFV_E_INVAL
+    assert call(V=16, K=32) == sfv.SFV_E_INVAL
+    assert call(N=0) == sfv.SFV_E_INVAL
+    assert call(branch=-1) == sfv.SFV_E_INVAL
+    assert call(M=-1) == sfv.SFV_E_INVAL
+    assert call(ptr=None) == sfv.SFV_E_INVAL
+
+
+def test_draft_tree_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    F = ctypes.c_float
+
+    def call(N=8, K=8, D=5, W=2, T=0.0, ptr=f):
+        return lib.sfv_draft_tree(ptr, f, f, f, N, K, D, W, F(T), ctypes.c_uint64(1), ctypes.c_uint64(2),
+                                  ctypes.c_int64(3), f, f, f, None)
+
+    assert call(D=64) == sfv.SFV_E_INVAL
+    assert call(D=-1) == sfv.SFV_E_INVAL
+    assert call(W=17) == sfv.SFV_E_INVAL
+    assert call(K=33) == sfv.SFV_E_INVAL
+    assert call(N=257) == sfv.SFV_E_INVAL
+    assert call(T=-1.0) == sfv.SFV_E_INVAL
+    assert call(T=float("inf")) == sfv.SFV_E_INVAL
+    assert call(ptr=None) == sfv.SFV_E_INVAL
