@@ -230,6 +230,47 @@ def main():
     fold_ratio = float(1.0 - rec[1:].mean()) if wl.B1 > 1 else 0.0
     gate_bytes = 2 * 2 * (wl.B1 - 1) * wl.N * wl.D + 4 * 5 * wl.B1 * wl.N
     del fa, h_layer
+
+    # Drafting the next tree from this pass's stale conditionals of the main
+    # branch: top-32 per masked position, then a best-first tree of B1-1
+    # drafts with 4 children per node.
+    from branch_verify_amd import sfv
+    K_top, D_tree, W_tree = 32, wl.B1 - 1, 4
+    top_ids = torch.zeros((wl.N, K_top), dtype=torch.int32, device="cuda")
+    top_val = torch.zeros((wl.N, K_top), dtype=torch.float32, device="cuda")
+    conf_pos = torch.zeros((wl.N,), dtype=torch.float32, device="cuda")
+    t_par = torch.zeros((D_tree + 1,), dtype=torch.int32, device="cuda")
+    t_st = torch.zeros((D_tree + 1, wl.N), dtype=torch.int32, device="cuda")
+    t_nd = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    root = xd["state"][0]
+
+    topk_wsb = sfv.sfv_stale_topk_workspace_bytes(step.M, wl.V, wl.N, K_top)
+    topk_ws = torch.empty(max(topk_wsb, 16), dtype=torch.uint8, device="cuda")
+
+    def draft_once():
+        sfv.sfv_stale_topk(step.logits, step.rows, step.conf, step.M, wl.V, wl.N, 0, K_top, top_ids, top_val,
+                           conf_pos, topk_ws, topk_wsb)
+        dev[1].record(stream)
+        sfv.sfv_draft_tree(root, top_ids, top_val, conf_pos, wl.N, K_top, D_tree, W_tree, wl.T, wl.seed,
+                           wl.step0 + 1, wl.pos0, t_par, t_st, t_nd)
+
+    dev = [None, torch.cuda.Event(enable_timing=True)]
+    for _ in range(3):
+        draft_once()
+    torch.cuda.synchronize()
+    dtimes = []
+    for s_ in range(a.steps):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        dev[1] = e1
+        e0.record(stream)
+        draft_once()
+        e2.record(stream)
+        dtimes.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    topk_us = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in dtimes])) * 1e3
+    tree_us = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in dtimes])) * 1e3
+    main_rows = int((x["state"][0] == -1).sum())
+    n_drafted = int(t_nd.item())
     ms_per_step = elapsed / a.steps * 1e3
     alg = algorithmic(wl, M)
     lm_bytes, lm_flop = alg["lm_head"]
@@ -270,6 +311,9 @@ def main():
                                "attention_us": fattn_us, "dense_attention_us": per["attention"],
                                "speedup_vs_dense": per["attention"] / (gate_us + fattn_us),
                                "gate_hbm_frac": gate_bytes / (gate_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    out["drafting"] = {"K": K_top, "D": D_tree, "W": W_tree, "topk_us": topk_us, "tree_us": tree_us,
+                       "main_masked_rows": main_rows, "drafts_built": n_drafted,
+                       "topk_hbm_frac": 2 * 4 * main_rows * wl.V / (topk_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
     out["commit_threshold"] = {"k_max": k_thr, "tau": tau_thr, "us": thr_us,
                                "positions_committed": thr_taken,
                                "hbm_frac": cb / (thr_us * 1e-6) / 1e9 / HBM_PEAK_GBS}

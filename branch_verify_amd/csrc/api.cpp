@@ -134,18 +134,37 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk, con
                     "sfv_attend_branches");
 }
 
-int sfv_stale_topk(const float* logits, const int32_t* rows, const float* conf, int M, int V, int N,
-                   int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos, void* stream) {
+int check_topk_dims(int M, int V, int N, int K) {
   if (N < 1 || N > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "N=%d not in [1, %d]", N, SFV_MAX_BLOCK);
   if (M < 0 || M > SFV_MAX_BRANCHES * N) return fail(SFV_E_INVAL, "M=%d out of range", M);
-  if (V < 1) return fail(SFV_E_INVAL, "V=%d < 1", V);
+  if (V < 1 || V >= (1 << 30)) return fail(SFV_E_INVAL, "V=%d out of range", V);
   if (K < 1 || K > SFV_MAX_TOPK || K > V) return fail(SFV_E_INVAL, "K=%d not in [1, min(%d, V)]", K, SFV_MAX_TOPK);
-  if (branch < 0 || branch >= SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "branch=%d out of range", branch);
   if ((double)M * V >= 9.0e15) return fail(SFV_E_INVAL, "too large");
-  if (M > 0 && (!logits || !rows || !conf || !top_ids || !top_logit || !conf_pos))
+  return SFV_OK;
+}
+
+int sfv_stale_topk_workspace_bytes(int M, int V, int N, int K, size_t* bytes) {
+  if (!bytes) return fail(SFV_E_INVAL, "bytes is NULL");
+  const int rc = check_topk_dims(M, V, N, K);
+  if (rc != SFV_OK) return rc;
+  *bytes = sfv::topk_plan(M, V, K).ws_bytes;
+  return ok();
+}
+
+int sfv_stale_topk(const float* logits, const int32_t* rows, const float* conf, int M, int V, int N,
+                   int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const int rc = check_topk_dims(M, V, N, K);
+  if (rc != SFV_OK) return rc;
+  if (branch < 0 || branch >= SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "branch=%d out of range", branch);
+  if (M > 0 && (!logits || !rows || !conf || !top_ids || !top_logit || !conf_pos || !workspace))
     return fail(SFV_E_INVAL, "null pointer");
+  const sfv::TopkPlan plan = sfv::topk_plan(M, V, K);
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
+  if ((uintptr_t)workspace % 16 != 0) return fail(SFV_E_INVAL, "workspace must be 16-byte aligned");
   return hip_status(sfv::launch_stale_topk(logits, rows, conf, M, V, N, branch, K, top_ids, top_logit, conf_pos,
-                                           (hipStream_t)stream),
+                                           workspace, plan, (hipStream_t)stream),
                     "sfv_stale_topk");
 }
 

@@ -73,9 +73,18 @@ hipError_t launch_match(const int32_t* state, const int32_t* next_state, const i
 
 hipError_t launch_selfcheck(double* out, hipStream_t stream);
 
+constexpr int kMaxTopk = 32;            // stale conditionals per position
+constexpr int kMaxTopkChunks = 16;      // workgroups per row of the stale top-K
+constexpr int kTopkChunkTarget = 4096;  // ids per chunk it aims for
+struct TopkPlan {
+  int S, C;  // chunks per row, ids per chunk
+  size_t ws_bytes;
+};
+TopkPlan topk_plan(int M, int V, int K);
+
 hipError_t launch_stale_topk(const float* logits, const int32_t* rows, const float* conf, int M, int V, int N,
-                             int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos,
-                             hipStream_t stream);
+                             int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos, void* ws,
+                             const TopkPlan& plan, hipStream_t stream);
 
 hipError_t launch_draft_tree(const int32_t* root, const int32_t* top_ids, const float* top_logit,
                              const float* conf, int N, int K, int D, int W, float temperature, uint64_t seed,

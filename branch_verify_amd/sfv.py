@@ -23,7 +23,7 @@ EXPORTS = [
     "sfv_last_error", "sfv_version", "sfv_attend_workspace_bytes", "sfv_attend_branches",
     "sfv_masked_rows", "sfv_lm_head", "sfv_commit_workspace_bytes", "sfv_commit",
     "sfv_match_tree", "sfv_selfcheck_bounds", "sfv_fold_gate", "sfv_attend_folded_workspace_bytes",
-    "sfv_attend_folded", "sfv_stale_topk", "sfv_draft_tree",
+    "sfv_attend_folded", "sfv_stale_topk_workspace_bytes", "sfv_stale_topk", "sfv_draft_tree",
 ]
 
 _lib = None
@@ -64,7 +64,8 @@ def load(path: str = LIB_PATH):
     lib.sfv_commit.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P, SZ, P]
     lib.sfv_match_tree.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
     lib.sfv_selfcheck_bounds.argtypes = [P, P]
-    lib.sfv_stale_topk.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P]
+    lib.sfv_stale_topk_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
+    lib.sfv_stale_topk.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, SZ, P]
     lib.sfv_draft_tree.argtypes = [P, P, P, P, I, I, I, I, F, U64, U64, I64, P, P, P, P]
     lib.sfv_fold_gate.argtypes = [P, P, I, I, I, F, P, P, P, P, P, P, P]
     lib.sfv_attend_folded_workspace_bytes.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
@@ -183,10 +184,17 @@ def sfv_attend_folded(q, k_blk, v_blk, k_ctx, v_ctx, B1, N, L, Hq, Hkv, d, softm
         _ptr(lse), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
-def sfv_stale_topk(logits, rows, conf, M, V, N, branch, K, top_ids, top_logit, conf_pos, stream=None):
+def sfv_stale_topk_workspace_bytes(M, V, N, K) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().sfv_stale_topk_workspace_bytes(M, V, N, K, ctypes.byref(out)))
+    return out.value
+
+
+def sfv_stale_topk(logits, rows, conf, M, V, N, branch, K, top_ids, top_logit, conf_pos, workspace,
+                   workspace_bytes, stream=None):
     return _check(load().sfv_stale_topk(
         _ptr(logits), _ptr(rows), _ptr(conf), M, V, N, branch, K, _ptr(top_ids), _ptr(top_logit),
-        _ptr(conf_pos), _stream(stream)))
+        _ptr(conf_pos), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def sfv_draft_tree(root, top_ids, top_logit, conf, N, K, D, W, temperature, seed, step0, pos0,

@@ -99,10 +99,14 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk,
  * positions with no row are left untouched.
  *   logits [M][V] fp32; rows [M] int32; conf [M] fp32
  *   top_ids [N][K] int32 out; top_logit [N][K] fp32 out; conf_pos [N] fp32 out
- * Supported: 1 <= K <= min(32, V).  One workgroup per row (two passes over it).
+ *   workspace: sfv_stale_topk_workspace_bytes(M, V, N, K) bytes, 16-byte aligned
+ * Supported: 1 <= K <= min(32, V), V < 2^30.  Up to 16 workgroups per row
+ * (two passes over their chunk), then one per row to merge.
  */
+int sfv_stale_topk_workspace_bytes(int M, int V, int N, int K, size_t* bytes);
 int sfv_stale_topk(const float* logits, const int32_t* rows, const float* conf, int M, int V, int N,
-                   int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos, void* stream);
+                   int branch, int K, int32_t* top_ids, float* top_logit, float* conf_pos,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Draft tree from stale conditionals.  SPOT, "Important context" (block
@@ -114,8 +118,9 @@ int sfv_stale_topk(const float* logits, const int32_t* rows, const float* conf, 
  * From root [N] (SFV_MASK = masked) with, per masked position n, its top-K
  * ids/logits and confidence c_n: a node u offers its W most confident masked
  * positions (c descending, ties to the lower position) as children; child
- * u+n has probability P(u) * c_n / sum_{m masked in u} c_m (fp64, the sum in
- * increasing m); nodes are added best-first (probability, then lower parent
+ * u+n has probability P(u) * c_n / sum_{m masked in u} c_m (fp64; the sum a
+ * pairwise tree over 256 leaves, leaf m = c_m or 0, level by level element
+ * 2j plus 2j+1); nodes are added best-first (probability, then lower parent
  * index, then lower position) until D drafts.  W = 0 or 1 gives the chain.
  * Drafted token at n from a node of depth d: T = 0, top_ids[n][0]; T > 0, the
  * id maximising fl32(fl32(l * fl32(1/T)) + g(seed, step0 + d, pos0 + n, id))

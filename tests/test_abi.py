@@ -196,8 +196,8 @@ def test_stale_topk_validation(lib):
     P = ctypes.c_void_p
     f = P(0x1000)
 
-    def call(M=4, V=512, N=8, branch=0, K=32, ptr=f):
-        return lib.sfv_stale_topk(ptr, f, f, M, V, N, branch, K, f, f, f, None)
+    def call(M=4, V=512, N=8, branch=0, K=32, ptr=f, ws=1 << 30, wsp=f):
+        return lib.sfv_stale_topk(ptr, f, f, M, V, N, branch, K, f, f, f, wsp, ws, None)
 
     assert call(K=0) == sfv.SFV_E_INVAL
     assert call(K=33) == sfv.SFV_E_INVAL
@@ -206,6 +206,11 @@ def test_stale_topk_validation(lib):
     assert call(branch=-1) == sfv.SFV_E_INVAL
     assert call(M=-1) == sfv.SFV_E_INVAL
     assert call(ptr=None) == sfv.SFV_E_INVAL
+    assert call(wsp=P(0x1008)) == sfv.SFV_E_INVAL
+    rc, need = _ws(lib.sfv_stale_topk_workspace_bytes, 4, 151936, 8, 32)
+    assert rc == sfv.SFV_OK and need == 4 * 16 * 32 * 8
+    assert call(V=151936, ws=need - 1) == sfv.SFV_E_WORKSPACE
+    assert _ws(lib.sfv_stale_topk_workspace_bytes, 4, 16, 8, 32)[0] == sfv.SFV_E_INVAL
 
 
 def test_draft_tree_validation(lib):

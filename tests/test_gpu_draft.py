@@ -30,7 +30,10 @@ def run_topk(lg, rows, conf, N, branch, K):
     ids = torch.full((N, K), -7, dtype=torch.int32, device="cuda")
     vals = torch.full((N, K), float("nan"), dtype=torch.float32, device="cuda")
     cpos = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
-    sfv.sfv_stale_topk(_dev(lg), _dev(rows.astype(np.int32)), _dev(conf), M, V, N, branch, K, ids, vals, cpos)
+    wsb = sfv.sfv_stale_topk_workspace_bytes(M, V, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    sfv.sfv_stale_topk(_dev(lg), _dev(rows.astype(np.int32)), _dev(conf), M, V, N, branch, K, ids, vals, cpos,
+                       ws, wsb)
     torch.cuda.synchronize()
     return ids.cpu().numpy(), vals.cpu().numpy(), cpos.cpu().numpy()
 
@@ -128,7 +131,10 @@ def test_drafted_chain_is_accepted_by_a_static_target(gpu_lib, T):
     ids = torch.zeros((N, V), dtype=torch.int32, device="cuda")
     vals = torch.zeros((N, V), dtype=torch.float32, device="cuda")
     cpos = torch.zeros((N,), dtype=torch.float32, device="cuda")
-    sfv.sfv_stale_topk(lg1, s1.rows, s1.conf, s1.M, V, N, 0, V if V <= 32 else 32, ids, vals, cpos)
+    Kt = V if V <= 32 else 32
+    wsb = sfv.sfv_stale_topk_workspace_bytes(s1.M, V, N, Kt)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    sfv.sfv_stale_topk(lg1, s1.rows, s1.conf, s1.M, V, N, 0, Kt, ids, vals, cpos, ws, wsb)
     parent = torch.zeros((D + 1,), dtype=torch.int32, device="cuda")
     states = torch.zeros((D + 1, N), dtype=torch.int32, device="cuda")
     nd = torch.zeros((1,), dtype=torch.int32, device="cuda")

@@ -99,9 +99,9 @@ def _brute_tree_nodes(root, conf, W):
         masked = [n for n in range(N) if root[n] == O.MASK and n not in path]
         if not masked:
             return
-        total = 0.0
-        for m in masked:
-            total += float(conf[m])
+        leaves = np.zeros(Dr.SUM_LEAVES)
+        leaves[masked] = conf[masked].astype(np.float64)
+        total = Dr.pairwise_sum(leaves)
         for n in [n for n in order if n not in path][:W]:
             p = (P * float(conf[n])) / total
             out.append((p, path + (n,)))
@@ -133,6 +133,19 @@ def test_tree_is_the_most_probable_nodes(W):
     for b in range(1, nd + 1):
         diff = np.flatnonzero(states[b] != states[parent[b]])
         assert diff.size == 1 and states[parent[b]][diff[0]] == O.MASK
+
+
+def test_pairwise_sum():
+    """Exact on integers; zero leaves change nothing; the tree order is the
+    level-by-level pairing (checked on values where the order matters)."""
+    x = np.arange(256, dtype=np.float64)
+    assert Dr.pairwise_sum(x) == 255 * 256 / 2
+    y = np.zeros(256)
+    y[[3, 17, 200]] = [1.5, 2.25, -0.75]
+    assert Dr.pairwise_sum(y) == 3.0
+    z = np.zeros(4)
+    z[:] = [1e16, 1.0, -1e16, 1.0]
+    assert Dr.pairwise_sum(z) == (1e16 + 1.0) + (-1e16 + 1.0)
 
 
 def test_tree_padding_and_probabilities_decrease():
