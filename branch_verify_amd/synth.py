@@ -23,6 +23,7 @@ Recipe (every tensor has its own numpy stream, so any subset can be drawn):
   streams [seed, 16, c]   W rows in chunks of 4096                N(0, w_std)
   streams [seed, 17, 18]  layer-input hidden states of the fold gate (below)
   stream [seed, 19, c]    stand-in fp32 logits for the commit (draw_logits)
+  stream [seed, 20]       drafted blocks for rejection sampling (draw_trays)
 All floats are drawn in fp32 and rounded to bfloat16 (round to nearest even).
 
 Layer-input hidden states for SpecFold's parent-child gate (Sec. 3.1
@@ -252,6 +253,28 @@ def draw_logits(M: int, V: int, seed: int, chunk: int = 64) -> np.ndarray:
         sharp = np.exp(rng.uniform(np.log(0.5), np.log(8.0), (rows, 1))).astype(np.float32)
         out[c0:c0 + rows] = rng.standard_normal((rows, V), dtype=np.float32) * sharp
     return out
+
+
+def draw_trays(n_trays: int, B: int, V: int, seed: int, T: float = 1.0, drift: float = 0.8):
+    """Drafted blocks for rejection-sampling verification (stream [seed, 20]):
+    target logits [n][B+1][V] (draw_logits), a proposal q [n][B][V] = the
+    softmax of the target's logits at temperature T (1 when T = 0) plus
+    N(0, drift^2) noise per entry (fp32, normalised), and tokens [n][B] drawn
+    from q.  Returns (logits, q, tokens)."""
+    rng = _rng(seed, 20)
+    logits = draw_logits(n_trays * (B + 1), V, seed + 7919).reshape(n_trays, B + 1, V)
+    q = np.empty((n_trays, B, V), dtype=np.float32)
+    tokens = np.empty((n_trays, B), dtype=np.int32)
+    t_eff = T if T > 0 else 1.0
+    for j in range(n_trays):
+        z = logits[j, :B].astype(np.float64) / t_eff + drift * rng.standard_normal((B, V))
+        z -= z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        qj = e / e.sum(axis=1, keepdims=True)
+        q[j] = qj.astype(np.float32)
+        g = rng.gumbel(size=(B, V))
+        tokens[j] = np.argmax(np.log(np.maximum(qj, 1e-300)) + g, axis=1)
+    return logits, q, tokens
 
 
 def masked_count(state: np.ndarray) -> int:

@@ -247,13 +247,14 @@ def philox4x64_10(ctr, key):
         return np.stack([c0, c1, c2, c3], axis=-1)
 
 
-def noise_words(seed: int, step: int, pos: int, v) -> np.ndarray:
+def noise_words(seed: int, step: int, pos: int, v, stream: int = 0) -> np.ndarray:
     """32-bit noise word for (seed, step, position, vocab id).
 
     Counter-based hash (SPOT, coupled-noise match: target and drafter share
     per-position Gumbel noise).  Key = (seed, 0); counter = (v >> 3, position,
-    step, 0), all as unsigned 64-bit; output word (v & 7) >> 1 of the four,
-    low half for even v and high half for odd v."""
+    step, stream), all as unsigned 64-bit; output word (v & 7) >> 1 of the
+    four, low half for even v and high half for odd v.  Stream 0 is the
+    commit's noise; other streams are independent draws for other uses."""
     v = np.asarray(v, dtype=np.int64)
     m64 = (1 << 64) - 1
     blocks, which = np.unique(v >> 3, return_inverse=True)   # one call per 8 ids
@@ -261,6 +262,7 @@ def noise_words(seed: int, step: int, pos: int, v) -> np.ndarray:
     ctr[:, 0] = blocks.astype(np.uint64)
     ctr[:, 1] = np.uint64(int(pos) & m64)
     ctr[:, 2] = np.uint64(int(step) & m64)
+    ctr[:, 3] = np.uint64(int(stream) & m64)
     key = np.array([int(seed) & m64, 0], dtype=np.uint64)
     out = philox4x64_10(ctr, key)
     word = out[which.reshape(v.shape), (v & 7) >> 1]
