@@ -26,6 +26,7 @@ SOURCES = {
     "match.hip": [],
     "fold.hip": ["-ffp-contract=off"],
     "draft.hip": ["-ffp-contract=off"],
+    "reject.hip": ["-ffp-contract=off"],
 }
 
 COMMON = [

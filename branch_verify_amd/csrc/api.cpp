@@ -234,6 +234,72 @@ int sfv_attend_folded(const void* q, const void* k_blk, const void* v_blk, const
                     "sfv_attend_folded");
 }
 
+int sfv_attend_trays(const void* q, const void* k_blk, const void* v_blk, const void* k_ctx, const void* v_ctx,
+                     int B1, int N, int L, int Hq, int Hkv, int d, float softmax_scale, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_attn_dims(B1, N, L, Hq, Hkv, d);
+  if (rc != SFV_OK) return rc;
+  if (!q || !k_blk || !v_blk || !o || !lse) return fail(SFV_E_INVAL, "null tensor pointer");
+  if (L > 0 && (!k_ctx || !v_ctx)) return fail(SFV_E_INVAL, "null context pointer with L=%d", L);
+  if (!std::isfinite(softmax_scale)) return fail(SFV_E_INVAL, "softmax_scale is not finite");
+  const sfv::AttnPlan plan = sfv::attn_plan(B1, N, L, Hq, Hkv, d);
+  if (workspace_bytes < plan.ws_bytes) {
+    return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
+  }
+  if (plan.ws_bytes > 0 && !workspace) return fail(SFV_E_INVAL, "workspace is NULL");
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_blk | (uintptr_t)v_blk | (uintptr_t)k_ctx |
+                       (uintptr_t)v_ctx | (uintptr_t)o | (uintptr_t)workspace;
+  if (al % 16 != 0) return fail(SFV_E_INVAL, "tensor pointers must be 16-byte aligned");
+  return hip_status(sfv::launch_attention(q, k_blk, v_blk, k_ctx, v_ctx, B1, N, L, Hq, Hkv, d, softmax_scale,
+                                          o, lse, workspace, plan, (hipStream_t)stream, nullptr, nullptr,
+                                          nullptr, nullptr, true),
+                    "sfv_attend_trays");
+}
+
+int check_reject_dims(int n_trays, int B, int V) {
+  if (n_trays < 1 || n_trays > SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "n_trays=%d not in [1, %d]", n_trays,
+                                                              SFV_MAX_BRANCHES);
+  if (B < 1 || B > SFV_MAX_BLOCK) return fail(SFV_E_INVAL, "B=%d not in [1, %d]", B, SFV_MAX_BLOCK);
+  if (V < 1 || V >= (1 << 30)) return fail(SFV_E_INVAL, "V=%d out of range", V);
+  if ((double)n_trays * (B + 1) * V >= 9.0e15) return fail(SFV_E_INVAL, "too large");
+  return SFV_OK;
+}
+
+int sfv_reject_workspace_bytes(int n_trays, int B, int V, size_t* bytes) {
+  if (!bytes) return fail(SFV_E_INVAL, "bytes is NULL");
+  const int rc = check_reject_dims(n_trays, B, V);
+  if (rc != SFV_OK) return rc;
+  *bytes = sfv::reject_plan(n_trays, B, V).ws_bytes;
+  return ok();
+}
+
+int sfv_reject_verify(const float* logits, const float* q, const int32_t* tokens, int n_trays, int B, int V,
+                      float temperature, uint64_t seed, uint64_t step0, int64_t pos0, int32_t* n_accept,
+                      int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_reject_dims(n_trays, B, V);
+  if (rc != SFV_OK) return rc;
+  if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(SFV_E_INVAL, "temperature must be >= 0");
+  if (!logits || !q || !tokens || !n_accept || !next_token || !workspace) return fail(SFV_E_INVAL, "null pointer");
+  const sfv::RejectPlan plan = sfv::reject_plan(n_trays, B, V);
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
+  if ((uintptr_t)workspace % 256 != 0) return fail(SFV_E_INVAL, "workspace must be 256-byte aligned");
+  return hip_status(sfv::launch_reject(logits, q, tokens, n_trays, B, V, temperature, seed, step0, pos0, n_accept,
+                                       next_token, workspace, plan, (hipStream_t)stream),
+                    "sfv_reject_verify");
+}
+
+int sfv_match_trays(const int32_t* n_accept, const int32_t* next_token, int verified, const int32_t* tray_k,
+                    const int32_t* tray_alt, int n_prepared, int32_t* served, void* stream) {
+  if (verified < 0 || verified >= SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "verified=%d out of range", verified);
+  if (n_prepared < 0 || n_prepared > (1 << 20)) return fail(SFV_E_INVAL, "n_prepared=%d out of range", n_prepared);
+  if (!n_accept || !next_token || !served || (n_prepared > 0 && (!tray_k || !tray_alt)))
+    return fail(SFV_E_INVAL, "null pointer");
+  return hip_status(sfv::launch_match_trays(n_accept, next_token, verified, tray_k, tray_alt, n_prepared, served,
+                                            (hipStream_t)stream),
+                    "sfv_match_trays");
+}
+
 int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t* count, void* stream) {
   if (!state || !rows || !count) return fail(SFV_E_INVAL, "null pointer");
   if (B1 < 1 || B1 > SFV_MAX_BRANCHES) return fail(SFV_E_INVAL, "B1=%d not in [1, %d]", B1, SFV_MAX_BRANCHES);

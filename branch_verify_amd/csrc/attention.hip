@@ -19,6 +19,9 @@
 //    the tile; a key is visible to a row only if both belong to one branch.
 //  * Long contexts are split into key ranges (split-KV) whose (m, l, O)
 //    states are merged by log-sum-exp in a second kernel.
+//  * With `causal`, a row sees the block keys of its branch only up to its
+//    own position (an autoregressive target verifying drafted trays, each
+//    tray a branch continuing the shared context).
 //  * Folded verification (SpecFold App. A.1 and B) runs the same kernel in
 //    two more modes.  kCtx: only the compacted recomputed slots, against the
 //    context keys alone, leaving their (m, l, O) states in the workspace
@@ -63,6 +66,7 @@ struct Params {
   int B1, N, L, Hq, Hkv, G;
   int rows_total, row_tiles, splits, chunk;
   float scale_log2;  // softmax scale * log2(e), applied inside the exp2
+  bool causal;       // block keys visible only up to the row's own position
 };
 
 template <int D>
@@ -308,7 +312,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
       int lo = 0, hi = cur.count;
       if (!cur.ctx) {
         lo = max(lo, (my_branch - i_lo) * p.N - cur.key0);
-        hi = min(hi, (my_branch - i_lo + 1) * p.N - cur.key0);
+        const int last = p.causal ? bn_q % p.N : p.N - 1;  // the row's last visible block position
+        hi = min(hi, (my_branch - i_lo) * p.N + last + 1 - cur.key0);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -564,8 +569,9 @@ hipError_t launch_attention(const void* q, const void* k_blk, const void* v_blk,
                             int Hq, int Hkv, int d, float scale, void* o, float* lse,
                             void* ws, const AttnPlan& plan, hipStream_t stream,
                             const int32_t* rec_rows, const int32_t* src, const int32_t* rec_count,
-                            const int32_t* rec_pos) {
+                            const int32_t* rec_pos, bool causal) {
   Params p;
+  p.causal = causal;
   p.qrows = rec_rows;
   p.src = src;
   p.count = rec_count;

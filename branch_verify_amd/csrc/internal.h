@@ -28,7 +28,8 @@ hipError_t launch_attention(const void* q, const void* k_blk, const void* v_blk,
                             int Hq, int Hkv, int d, float scale, void* o, float* lse,
                             void* ws, const AttnPlan& plan, hipStream_t stream,
                             const int32_t* rec_rows = nullptr, const int32_t* src = nullptr,
-                            const int32_t* rec_count = nullptr, const int32_t* rec_pos = nullptr);
+                            const int32_t* rec_count = nullptr, const int32_t* rec_pos = nullptr,
+                            bool causal = false);
 
 hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows,
                               int32_t* count, hipStream_t stream);
@@ -90,6 +91,29 @@ hipError_t launch_draft_tree(const int32_t* root, const int32_t* top_ids, const 
                              const float* conf, int N, int K, int D, int W, float temperature, uint64_t seed,
                              uint64_t step0, int64_t pos0, int32_t* parent, int32_t* states, int32_t* n_drafts,
                              hipStream_t stream);
+
+// Rejection-sampling verification of drafted trays.
+constexpr int kMaxRejectChunks = 16;
+constexpr int kRejectChunkTarget = 8192;
+struct RejectPlan {
+  int S, C;  // chunks per emitting row, ids per chunk
+  size_t ws_bytes;
+};
+struct RejectWs {
+  float* row_max;    // [n][B+1] max of the (scaled) logits
+  int* row_arg;      // [n][B+1] first index attaining it
+  double* row_sum;   // [n][B+1] sum exp(z - max), fp64
+  int* accept;       // [n][B+1] drafted token accepted (positions < B)
+  double* chunk_key; // [n][S]
+  int* chunk_id;     // [n][S]
+};
+RejectPlan reject_plan(int n, int B, int V);
+hipError_t launch_reject(const float* logits, const float* q, const int32_t* tokens, int n, int B, int V,
+                         float temperature, uint64_t seed, uint64_t step0, int64_t pos0, int32_t* n_accept,
+                         int32_t* next_token, void* ws, const RejectPlan& plan, hipStream_t stream);
+hipError_t launch_match_trays(const int32_t* n_accept, const int32_t* next_token, int verified,
+                              const int32_t* tray_k, const int32_t* tray_alt, int n_prepared, int32_t* served,
+                              hipStream_t stream);
 
 hipError_t launch_fold_gate(const void* H, const TreeArgs& tree, int N, int D, float delta,
                             int32_t* recompute, int32_t* src, int32_t* rec_rows, int32_t* rec_count,

@@ -5,8 +5,10 @@
 // per-position Gumbel noise, so given the noise every transition is
 // deterministic.  Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
 // numbers: as easy as 1, 2, 3", SC'11) keyed by (seed, 0) on the counter
-// (id >> 3, position, step, 0); id's word is half (id & 1) of output
-// (id & 7) >> 1; g = -ln(-ln u) with u = (word + 1/2) 2^-32.
+// (id >> 3, position, step, stream); id's word is half (id & 1) of output
+// (id & 7) >> 1; g = -ln(-ln u) with u = (word + 1/2) 2^-32.  Stream 0 is
+// the commit's and drafter's noise; streams 1 and 2 are the rejection
+// sampler's acceptance uniforms and residual/bonus draws.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,8 +37,8 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
 
 // The 8 noise words of ids 8*blk .. 8*blk+7: word j = half (j & 1) of output (j >> 1).
 __device__ __forceinline__ void noise_block(uint64_t seed, uint64_t step, uint64_t pos, uint64_t blk,
-                                            unsigned w[8]) {
-  uint64_t c[4] = {blk, pos, step, 0};
+                                            unsigned w[8], uint64_t stream = 0) {
+  uint64_t c[4] = {blk, pos, step, stream};
   philox4x64_10(c, seed, 0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -57,8 +59,9 @@ __device__ __forceinline__ double gumbel_exact_f64(unsigned w) {
 }
 
 // The noise word of one vocab id.
-__device__ __forceinline__ unsigned noise_word(uint64_t seed, uint64_t step, uint64_t pos, uint64_t id) {
-  uint64_t c[4] = {id >> 3, pos, step, 0};
+__device__ __forceinline__ unsigned noise_word(uint64_t seed, uint64_t step, uint64_t pos, uint64_t id,
+                                               uint64_t stream = 0) {
+  uint64_t c[4] = {id >> 3, pos, step, stream};
   philox4x64_10(c, seed, 0);
   const int j = (int)((id & 7) >> 1);
   const uint64_t w = j == 0 ? c[0] : j == 1 ? c[1] : j == 2 ? c[2] : c[3];

@@ -1,0 +1,325 @@
+// Verification of drafted trays by rejection sampling, and serving the
+// prepared tray that matches the verified prefix.
+//
+// D3D explainer ("D3D diffusion drafter -- Asynchronous speculative
+// decoding"): the target verifies a drafted block by rejection sampling with
+// the proposal probabilities, which keeps the target's distribution; trays
+// prepared for each plausible rejection point are served on a match.
+//
+// reject_stats_kernel: one workgroup per (tray, position) row of target
+// logits.  T > 0: z = fl32(l * invT), M = max z, S = sum exp(z - M) in fp64
+// (exact exp); at a drafted position the acceptance test u * q(x) < p(x)
+// with p(x) = exp(z_x - M) / S.  T = 0: the first argmax, and acceptance iff
+// the drafted token is it.
+// reject_sample_kernel: T > 0 only.  Each tray's emitting row (its first
+// rejection, else the bonus row) is cut into chunks; each chunk's best
+// Gumbel-max key over the residual ln(p - q) + g (or the bonus key z + g),
+// all in fp64.
+// reject_finalize_kernel: one wave per tray merges the chunks.
+// match_trays_kernel: one wave finds the lowest prepared tray matching.
+#include "common.h"
+#include "internal.h"
+#include "noise.h"
+
+namespace sfv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr uint64_t kStreamAccept = 1, kStreamSample = 2;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct RejectArgs {
+  const float* logits;    // [n][B+1][V]
+  const float* q;         // [n][B][V]
+  const int32_t* tokens;  // [n][B]
+  int n, B, V;
+  bool noisy;
+  float inv_t;
+  uint64_t seed, step0;
+  int64_t pos0;
+  int S, C;               // chunks per emitting row, ids per chunk
+  RejectWs ws;
+  int32_t* n_accept;
+  int32_t* next_token;
+};
+
+__device__ __forceinline__ bool better_d(double v, int i, double bv, int bi) {
+  return (v > bv) | ((v == bv) & (i < bi));
+}
+
+__device__ __forceinline__ void block_reduce_max_f(float& v, int& i, float* sv, int* si) {
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(i, o, kWave);
+    const bool take = (ov > v) | ((ov == v) & (oi < i));
+    v = take ? ov : v;
+    i = take ? oi : i;
+  }
+  if (lane == 0) {
+    sv[wave] = v;
+    si[wave] = i;
+  }
+  __syncthreads();
+  v = sv[0];
+  i = si[0];
+  for (int w = 1; w < kThreads / kWave; ++w) {
+    const bool take = (sv[w] > v) | ((sv[w] == v) & (si[w] < i));
+    v = take ? sv[w] : v;
+    i = take ? si[w] : i;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void reject_stats_kernel(RejectArgs a) {
+  __shared__ float s_v[kThreads / kWave];
+  __shared__ int s_i[kThreads / kWave];
+  __shared__ double s_d[kThreads / kWave];
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int row = blockIdx.x;  // j * (B + 1) + pos
+  const int j = row / (a.B + 1), pos = row % (a.B + 1);
+  const float* l = a.logits + (size_t)row * a.V;
+
+  // max (T > 0: of fl32(l * invT)) with the first index attaining it
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int v = t; v < a.V; v += kThreads) {
+    const float z = a.noisy ? l[v] * a.inv_t : l[v];
+    const bool take = (z > bv) | ((z == bv) & (v < bi));
+    bv = take ? z : bv;
+    bi = take ? v : bi;
+  }
+  block_reduce_max_f(bv, bi, s_v, s_i);
+  const float M = bv;
+  if (t == 0) {
+    a.ws.row_max[row] = M;
+    a.ws.row_arg[row] = bi;
+  }
+  if (!a.noisy) {
+    if (t == 0 && pos < a.B) a.ws.accept[row] = a.tokens[j * a.B + pos] == bi;
+    return;
+  }
+  double sum = 0.0;
+  for (int v = t; v < a.V; v += kThreads) sum += exp((double)(l[v] * a.inv_t) - (double)M);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+  if (lane == 0) s_d[wave] = sum;
+  __syncthreads();
+  if (t == 0) {
+    double S = 0.0;
+    for (int w = 0; w < kThreads / kWave; ++w) S += s_d[w];
+    a.ws.row_sum[row] = S;
+    if (pos < a.B) {
+      const int x = min(max(a.tokens[j * a.B + pos], 0), a.V - 1);  // tokens are in [0, V)
+      const double px = exp((double)(l[x] * a.inv_t) - (double)M) / S;
+      const unsigned w = noise_word(a.seed, a.step0 + (uint64_t)j, (uint64_t)(a.pos0 + pos), 0, kStreamAccept);
+      const double u = ((double)w + 0.5) * 2.3283064365386962890625e-10;
+      const double qx = (double)a.q[((size_t)j * a.B + pos) * a.V + x];
+      a.ws.accept[row] = u * qx < px;
+    }
+  }
+}
+
+// First rejected position of tray j (B if every drafted token passes).
+__device__ __forceinline__ int first_reject(const RejectArgs& a, int j) {
+  int r = a.B;
+  for (int t = a.B - 1; t >= 0; --t)
+    if (!a.ws.accept[j * (a.B + 1) + t]) r = t;
+  return r;
+}
+
+__global__ __launch_bounds__(kThreads) void reject_sample_kernel(RejectArgs a) {
+  __shared__ double s_k[kThreads / kWave];
+  __shared__ int s_i[kThreads / kWave];
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int j = blockIdx.x / a.S, sc = blockIdx.x % a.S;
+  const int r = first_reject(a, j);
+  const int row = j * (a.B + 1) + r;
+  const float* l = a.logits + (size_t)row * a.V;
+  const float* qr = a.q + ((size_t)j * a.B + min(r, a.B - 1)) * a.V;
+  const bool residual = r < a.B;
+  const float M = a.ws.row_max[row];
+  const double S = a.ws.row_sum[row];
+  const uint64_t step = a.step0 + (uint64_t)j, posn = (uint64_t)(a.pos0 + r);
+  const int c0 = sc * a.C, c1 = min(a.V, c0 + a.C);
+  double bk = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  // each thread takes runs of 8 consecutive ids (one Philox call per run)
+  for (int base = c0 + 8 * t; base < c1; base += 8 * kThreads) {
+    unsigned w[8];
+    noise_block(a.seed, step, posn, (uint64_t)(base >> 3), w, kStreamSample);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int v = base + e;
+      if (v >= c1) continue;
+      const double z = (double)(l[v] * a.inv_t);
+      double key;
+      if (residual) {
+        const double res = exp(z - (double)M) / S - (double)qr[v];
+        if (!(res > 0.0)) continue;
+        key = log(res);
+      } else {
+        key = z;
+      }
+      key += gumbel_exact_f64(w[e]);
+      const bool take = better_d(key, v, bk, bi);
+      bk = take ? key : bk;
+      bi = take ? v : bi;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ok = __shfl_xor(bk, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    const bool take = better_d(ok, oi, bk, bi);
+    bk = take ? ok : bk;
+    bi = take ? oi : bi;
+  }
+  if (lane == 0) {
+    s_k[wave] = bk;
+    s_i[wave] = bi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int w2 = 1; w2 < kThreads / kWave; ++w2) {
+      const bool take = better_d(s_k[w2], s_i[w2], bk, bi);
+      bk = take ? s_k[w2] : bk;
+      bi = take ? s_i[w2] : bi;
+    }
+    a.ws.chunk_key[j * a.S + sc] = bk;
+    a.ws.chunk_id[j * a.S + sc] = bi;
+  }
+}
+
+__global__ __launch_bounds__(kWave) void reject_finalize_kernel(RejectArgs a) {
+  const int lane = threadIdx.x;
+  const int j = blockIdx.x;
+  const int r = first_reject(a, j);
+  int tok;
+  if (!a.noisy) {
+    tok = a.ws.row_arg[j * (a.B + 1) + r];
+  } else {
+    // (an empty residual, p <= q everywhere by rounding, emits the first argmax of z)
+    double bk = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int c = lane; c < a.S; c += kWave) {
+      const double k = a.ws.chunk_key[j * a.S + c];
+      const int i = a.ws.chunk_id[j * a.S + c];
+      const bool take = better_d(k, i, bk, bi);
+      bk = take ? k : bk;
+      bi = take ? i : bi;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ok = __shfl_xor(bk, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      const bool take = better_d(ok, oi, bk, bi);
+      bk = take ? ok : bk;
+      bi = take ? oi : bi;
+    }
+    tok = bi == 0x7FFFFFFF ? a.ws.row_arg[j * (a.B + 1) + r] : bi;
+  }
+  if (lane == 0) {
+    a.n_accept[j] = r;
+    a.next_token[j] = tok;
+  }
+}
+
+__global__ __launch_bounds__(kWave) void match_trays_kernel(const int32_t* n_accept, const int32_t* next_token,
+                                                            int verified, const int32_t* tray_k,
+                                                            const int32_t* tray_alt, int n_prepared,
+                                                            int32_t* served) {
+  const int lane = threadIdx.x;
+  const int a0 = n_accept[verified], c0 = next_token[verified];
+  int found = -1;
+  for (int b0 = 0; b0 < n_prepared; b0 += kWave) {
+    const int k = b0 + lane;
+    const bool hit = k < n_prepared && tray_k[k] == a0 && tray_alt[k] == c0;
+    const unsigned long long bal = __ballot(hit);
+    if (bal != 0ull) {
+      found = b0 + __ffsll((long long)bal) - 1;
+      break;
+    }
+  }
+  if (lane == 0) served[0] = found;
+}
+
+}  // namespace
+
+RejectPlan reject_plan(int n, int B, int V) {
+  RejectPlan pl;
+  int S = (V + kRejectChunkTarget - 1) / kRejectChunkTarget;
+  S = S < 1 ? 1 : (S > kMaxRejectChunks ? kMaxRejectChunks : S);
+  int C = (V + S - 1) / S;
+  C = (C + 7) / 8 * 8;  // runs of 8 ids stay in one chunk
+  S = (V + C - 1) / C;
+  pl.S = S;
+  pl.C = C;
+  const size_t rows = (size_t)n * (B + 1);
+  pl.ws_bytes = align256(rows * sizeof(float)) + align256(rows * sizeof(int)) + align256(rows * sizeof(double)) +
+                align256(rows * sizeof(int)) + align256((size_t)n * S * sizeof(double)) +
+                align256((size_t)n * S * sizeof(int));
+  return pl;
+}
+
+RejectWs reject_ws(void* base, int n, int B, const RejectPlan& plan) {
+  char* p = (char*)base;
+  const size_t rows = (size_t)n * (B + 1);
+  RejectWs ws;
+  ws.row_max = (float*)p;
+  p += align256(rows * sizeof(float));
+  ws.row_arg = (int*)p;
+  p += align256(rows * sizeof(int));
+  ws.row_sum = (double*)p;
+  p += align256(rows * sizeof(double));
+  ws.accept = (int*)p;
+  p += align256(rows * sizeof(int));
+  ws.chunk_key = (double*)p;
+  p += align256((size_t)n * plan.S * sizeof(double));
+  ws.chunk_id = (int*)p;
+  return ws;
+}
+
+hipError_t launch_reject(const float* logits, const float* q, const int32_t* tokens, int n, int B, int V,
+                         float temperature, uint64_t seed, uint64_t step0, int64_t pos0, int32_t* n_accept,
+                         int32_t* next_token, void* ws, const RejectPlan& plan, hipStream_t stream) {
+  RejectArgs a;
+  a.logits = logits;
+  a.q = q;
+  a.tokens = tokens;
+  a.n = n;
+  a.B = B;
+  a.V = V;
+  a.noisy = temperature != 0.f;
+  a.inv_t = a.noisy ? 1.0f / temperature : 1.f;
+  a.seed = seed;
+  a.step0 = step0;
+  a.pos0 = pos0;
+  a.S = plan.S;
+  a.C = plan.C;
+  a.ws = reject_ws(ws, n, B, plan);
+  a.n_accept = n_accept;
+  a.next_token = next_token;
+  hipLaunchKernelGGL(reject_stats_kernel, dim3(n * (B + 1)), dim3(kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.noisy) {
+    hipLaunchKernelGGL(reject_sample_kernel, dim3(n * plan.S), dim3(kThreads), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(reject_finalize_kernel, dim3(n), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_match_trays(const int32_t* n_accept, const int32_t* next_token, int verified,
+                              const int32_t* tray_k, const int32_t* tray_alt, int n_prepared, int32_t* served,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(match_trays_kernel, dim3(1), dim3(kWave), 0, stream, n_accept, next_token, verified, tray_k,
+                     tray_alt, n_prepared, served);
+  return hipGetLastError();
+}
+
+}  // namespace sfv

@@ -24,6 +24,7 @@ EXPORTS = [
     "sfv_masked_rows", "sfv_lm_head", "sfv_commit_workspace_bytes", "sfv_commit",
     "sfv_match_tree", "sfv_selfcheck_bounds", "sfv_fold_gate", "sfv_attend_folded_workspace_bytes",
     "sfv_attend_folded", "sfv_stale_topk_workspace_bytes", "sfv_stale_topk", "sfv_draft_tree",
+    "sfv_attend_trays", "sfv_reject_workspace_bytes", "sfv_reject_verify", "sfv_match_trays",
 ]
 
 _lib = None
@@ -59,6 +60,10 @@ def load(path: str = LIB_PATH):
     lib.sfv_attend_workspace_bytes.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_attend_branches.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, SZ, P]
     lib.sfv_masked_rows.argtypes = [P, I, I, P, P, P]
+    lib.sfv_reject_workspace_bytes.argtypes = [I, I, I, ctypes.POINTER(SZ)]
+    lib.sfv_reject_verify.argtypes = [P, P, P, I, I, I, F, U64, U64, I64, P, P, P, SZ, P]
+    lib.sfv_match_trays.argtypes = [P, P, I, P, P, I, P, P]
+    lib.sfv_attend_trays.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, SZ, P]
     lib.sfv_lm_head.argtypes = [P, P, I, I, P, I, I, P, P]
     lib.sfv_commit_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_commit.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P, SZ, P]
@@ -113,6 +118,14 @@ def sfv_attend_workspace_bytes(B1, N, L, Hq, Hkv, d) -> int:
 def sfv_attend_branches(q, k_blk, v_blk, k_ctx, v_ctx, B1, N, L, Hq, Hkv, d, softmax_scale,
                         o, lse, workspace=None, workspace_bytes=0, stream=None):
     return _check(load().sfv_attend_branches(
+        _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx), B1, N, L, Hq, Hkv, d,
+        float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+        _stream(stream)))
+
+
+def sfv_attend_trays(q, k_blk, v_blk, k_ctx, v_ctx, B1, N, L, Hq, Hkv, d, softmax_scale, o, lse,
+                     workspace=None, workspace_bytes=0, stream=None):
+    return _check(load().sfv_attend_trays(
         _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx), B1, N, L, Hq, Hkv, d,
         float(softmax_scale), _ptr(o), _ptr(lse), _ptr(workspace), int(workspace_bytes),
         _stream(stream)))
@@ -203,3 +216,23 @@ def sfv_draft_tree(root, top_ids, top_logit, conf, N, K, D, W, temperature, seed
         _ptr(root), _ptr(top_ids), _ptr(top_logit), _ptr(conf), N, K, D, W, float(temperature),
         int(seed) & (2**64 - 1), int(step0) & (2**64 - 1), int(pos0), _ptr(parent), _ptr(states),
         _ptr(n_drafts), _stream(stream)))
+
+
+def sfv_reject_workspace_bytes(n_trays, B, V) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().sfv_reject_workspace_bytes(n_trays, B, V, ctypes.byref(out)))
+    return out.value
+
+
+def sfv_reject_verify(logits, q, tokens, n_trays, B, V, temperature, seed, step0, pos0, n_accept,
+                      next_token, workspace, workspace_bytes, stream=None):
+    return _check(load().sfv_reject_verify(
+        _ptr(logits), _ptr(q), _ptr(tokens), n_trays, B, V, float(temperature),
+        int(seed) & (2**64 - 1), int(step0) & (2**64 - 1), int(pos0), _ptr(n_accept),
+        _ptr(next_token), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def sfv_match_trays(n_accept, next_token, verified, tray_k, tray_alt, n_prepared, served, stream=None):
+    return _check(load().sfv_match_trays(
+        _ptr(n_accept), _ptr(next_token), verified, _ptr(tray_k), _ptr(tray_alt), n_prepared,
+        _ptr(served), _stream(stream)))

@@ -88,6 +88,62 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Causal attention of drafted trays for an autoregressive target.  D3D
+ * explainer: the target verifies each prepared tray (a continuation of the
+ * shared prefix) in one packed pass.
+ *
+ * As sfv_attend_branches (branch = tray, position = token of the tray), but
+ * the row at position n of tray i sees the L context keys and the block keys
+ * of tray i at positions 0..n only.  Same shapes, dtypes, workspace
+ * (sfv_attend_workspace_bytes) and limits.
+ */
+int sfv_attend_trays(const void* q, const void* k_blk, const void* v_blk,
+                     const void* k_ctx, const void* v_ctx,
+                     int B1, int N, int L, int Hq, int Hkv, int d, float softmax_scale,
+                     void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Rejection-sampling verification of drafted trays for an autoregressive
+ * target.  D3D explainer: verification by rejection sampling with the
+ * proposal probabilities, the standard rule that preserves the target's
+ * distribution.
+ *
+ * For tray j (noise step step0 + j) with drafted tokens x_0..x_{B-1}:
+ *   T > 0: p_t = softmax(fl32(l_t * fl32(1/T))) in fp64 (exact exp);
+ *   x_t is accepted iff u_t * q_t(x_t) < p_t(x_t), u_t = (w + 1/2) 2^-32 with
+ *   w the noise word of id 0 on stream 1 at position pos0 + t; a = the first
+ *   rejected t (B if none).  a < B emits argmax over v with p_a(v) > q_a(v)
+ *   of ln(p_a(v) - q_a(v)) + g(v); a = B emits argmax_v fl32(l_B(v) / T) +
+ *   g(v); g = -ln(-ln u) in fp64 from stream 2 at position pos0 + a; ties to
+ *   the lower id; an empty residual emits the first argmax of fl32(l_a / T).
+ *   T = 0: x_t accepted iff it is the first argmax of l_t; emits the first
+ *   argmax of l_a.
+ *   logits [n_trays][B+1][V] fp32 (the target's distributions at the B
+ *   drafted positions and the bonus position); q [n_trays][B][V] fp32 (the
+ *   drafter's probabilities); tokens [n_trays][B] int32
+ *   n_accept [n_trays] int32 out (a); next_token [n_trays] int32 out
+ *   workspace: sfv_reject_workspace_bytes(n_trays, B, V), 256-byte aligned
+ * Supported: 1 <= n_trays <= 64, 1 <= B <= 256, T >= 0 finite.
+ */
+int sfv_reject_workspace_bytes(int n_trays, int B, int V, size_t* bytes);
+int sfv_reject_verify(const float* logits, const float* q, const int32_t* tokens, int n_trays, int B, int V,
+                      float temperature, uint64_t seed, uint64_t step0, int64_t pos0, int32_t* n_accept,
+                      int32_t* next_token, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Serving a prepared tray.  D3D explainer: each prepared tray extends the
+ * prefix by the tokens accepted before a rejection point and another token
+ * there; the tray matching the verified prefix is served (a cache hit).
+ *
+ * served[0] = the lowest k with tray_k[k] == n_accept[verified] and
+ * tray_alt[k] == next_token[verified], or -1 (a miss).
+ *   n_accept, next_token: as from sfv_reject_verify; tray_k, tray_alt
+ *   [n_prepared] int32 (device); served [1] int32 out.
+ */
+int sfv_match_trays(const int32_t* n_accept, const int32_t* next_token, int verified, const int32_t* tray_k,
+                    const int32_t* tray_alt, int n_prepared, int32_t* served, void* stream);
+
+/*
  * Stale conditionals for drafting.  SPOT, "How does SPOT draft and verify?"
  * (the drafter reads the target's latest top-32 probabilities at each masked
  * position) and "Important context" (stale conditionals).

@@ -24,7 +24,9 @@ Readings (the page states the rule but not its arithmetic):
     max(0, p - q) normalised: the Gumbel-max argmax_v ln(p_v - q_v) + g_v over
     v with p_v > q_v, g in fp64 from noise stream 2 at position pos0 + a.  If
     all B pass, the bonus token is argmax_v fl32(l_v invT) + g_v (stream 2,
-    position pos0 + B).  Ties go to the lower id.
+    position pos0 + B).  Ties go to the lower id.  An empty residual (p <= q
+    everywhere, possible only by rounding) emits the first argmax of
+    fl32(l invT).
   * T = 0: x is accepted iff it is the first argmax of l; the emitted token is
     the first argmax at position a (or B).
   * The served tray is the lowest-indexed tray whose (rejection point,
@@ -102,6 +104,8 @@ def verify_tray(logits, q, tokens, T: float, seed: int, step: int, pos0: int):
     if a < B:
         r = target_probs(logits[a], T) - q[a].astype(np.float64)
         pos = r > 0
+        if not pos.any():  # p <= q everywhere, possible only by rounding
+            return a, first_argmax(scaled_logits(logits[a], T))
         keys = np.where(pos, np.log(np.where(pos, r, 1.0)) + g, -np.inf)
         return a, _argmax_first(keys, pos)
     return a, _argmax_first(scaled_logits(logits[B], T) + g)
@@ -125,3 +129,37 @@ def match_tray(accepted: int, token: int, tray_k, tray_alt) -> int:
         if int(tray_k[j]) == accepted and int(tray_alt[j]) == token:
             return j
     return -1
+
+
+def tray_attention(q, k_blk, v_blk, k_ctx, v_ctx, scale):
+    """Attention of an autoregressive target over drafted trays ([D3D] the
+    target verifies the prepared trays in one packed pass): each tray i
+    continues the shared context, so position n of tray i attends the L
+    context keys and the tray's block keys 0..n.  Shapes as oracle.attention;
+    fp64.  Returns o [B1][N][Hq][d], lse [B1][N][Hq] (natural log)."""
+    q = np.asarray(q, np.float64)
+    k_blk = np.asarray(k_blk, np.float64)
+    v_blk = np.asarray(v_blk, np.float64)
+    k_ctx = np.asarray(k_ctx, np.float64)
+    v_ctx = np.asarray(v_ctx, np.float64)
+    B1, N, Hq, d = q.shape
+    Hkv = k_blk.shape[2]
+    G = Hq // Hkv
+    L = k_ctx.shape[1]
+    o = np.empty((B1, N, Hq, d))
+    lse = np.empty((B1, N, Hq))
+    for i in range(B1):
+        for h in range(Hq):
+            g = h // G
+            K = np.concatenate([k_ctx[g], k_blk[i, :, g]], axis=0)
+            V = np.concatenate([v_ctx[g], v_blk[i, :, g]], axis=0)
+            s = (q[i, :, h, :] @ K.T) * scale                  # [N][L+N]
+            visible = np.ones_like(s, dtype=bool)
+            visible[:, L:] = np.tril(np.ones((N, N), dtype=bool))
+            s = np.where(visible, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            Z = e.sum(axis=1, keepdims=True)
+            o[i, :, h, :] = (e @ V) / Z
+            lse[i, :, h] = (m + np.log(Z))[:, 0]
+    return o, lse

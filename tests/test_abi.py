@@ -230,3 +230,36 @@ def test_draft_tree_validation(lib):
     assert call(T=-1.0) == sfv.SFV_E_INVAL
     assert call(T=float("inf")) == sfv.SFV_E_INVAL
     assert call(ptr=None) == sfv.SFV_E_INVAL
+
+
+def test_reject_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    F = ctypes.c_float
+
+    def call(n=4, B=16, V=512, T=1.0, ptr=f, ws=1 << 30, wsp=P(0x10000)):
+        return lib.sfv_reject_verify(ptr, f, f, n, B, V, F(T), ctypes.c_uint64(1), ctypes.c_uint64(2),
+                                     ctypes.c_int64(3), f, f, wsp, ws, None)
+
+    assert call(n=0) == sfv.SFV_E_INVAL
+    assert call(n=65) == sfv.SFV_E_INVAL
+    assert call(B=0) == sfv.SFV_E_INVAL
+    assert call(B=257) == sfv.SFV_E_INVAL
+    assert call(T=-0.5) == sfv.SFV_E_INVAL
+    assert call(T=float("nan")) == sfv.SFV_E_INVAL
+    assert call(ptr=None) == sfv.SFV_E_INVAL
+    assert call(wsp=P(0x10010)) == sfv.SFV_E_INVAL
+    rc, need = _ws(lib.sfv_reject_workspace_bytes, 4, 16, 151936)
+    assert rc == sfv.SFV_OK and need > 0
+    assert call(V=151936, ws=need - 1) == sfv.SFV_E_WORKSPACE
+    assert lib.sfv_match_trays(f, f, -1, f, f, 3, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_match_trays(f, f, 0, None, f, 3, f, None) == sfv.SFV_E_INVAL
+
+
+def test_attend_trays_validation(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    args = [fake] * 5 + [3, 8, 64, 4, 2, 32, ctypes.c_float(0.17), fake, fake]
+    assert lib.sfv_attend_trays(None, *args[1:], None, 0, None) == sfv.SFV_E_INVAL
+    bad = list(args); bad[10] = 96
+    assert lib.sfv_attend_trays(*bad, None, 0, None) == sfv.SFV_E_UNSUPPORTED

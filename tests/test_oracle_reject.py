@@ -118,3 +118,40 @@ def test_noise_streams_are_independent():
     b = O.noise_words(1, 2, 3, np.arange(64), stream=1)
     assert not np.array_equal(a, b)
     assert np.array_equal(a, O.noise_words(1, 2, 3, np.arange(64)))
+
+
+def _qkv(rng, B1, N, L, Hq, Hkv, d):
+    f = lambda *s: rng.standard_normal(s)
+    return f(B1, N, Hq, d), f(B1, N, Hkv, d), f(B1, N, Hkv, d), f(Hkv, L, d), f(Hkv, L, d)
+
+
+def test_tray_attention_against_torch_masked_sdpa():
+    import torch
+    rng = np.random.default_rng(11)
+    B1, N, L, Hq, Hkv, d = 3, 5, 7, 4, 2, 8
+    q, kb, vb, kc, vc = _qkv(rng, B1, N, L, Hq, Hkv, d)
+    o, lse = R.tray_attention(q, kb, vb, kc, vc, 0.4)
+    G = Hq // Hkv
+    mask = torch.ones(N, L + N, dtype=torch.bool)
+    mask[:, L:] = torch.tril(torch.ones(N, N, dtype=torch.bool))
+    for i in range(B1):
+        for h in range(Hq):
+            g = h // G
+            K = torch.from_numpy(np.concatenate([kc[g], kb[i, :, g]]))
+            V = torch.from_numpy(np.concatenate([vc[g], vb[i, :, g]]))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[i, :, h])[None], K[None], V[None], attn_mask=mask[None], scale=0.4)[0]
+            np.testing.assert_allclose(o[i, :, h], ref.numpy(), atol=1e-12)
+
+
+def test_tray_attention_last_position_sees_the_whole_tray():
+    rng = np.random.default_rng(12)
+    B1, N, L, Hq, Hkv, d = 2, 6, 9, 2, 1, 8
+    q, kb, vb, kc, vc = _qkv(rng, B1, N, L, Hq, Hkv, d)
+    o, lse = R.tray_attention(q, kb, vb, kc, vc, 0.3)
+    o2, lse2 = O.attention(q, kb, vb, kc, vc, 0.3)
+    np.testing.assert_allclose(o[:, -1], o2[:, -1], atol=1e-12)
+    np.testing.assert_allclose(lse[:, -1], lse2[:, -1], rtol=1e-13)
+    # position 0 sees the context and itself only
+    o0, _ = O.attention(q[:, :1], kb[:, :1], vb[:, :1], kc, vc, 0.3)
+    np.testing.assert_allclose(o[:, 0], o0[:, 0], atol=1e-12)
