@@ -271,6 +271,55 @@ def main():
     tree_us = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in dtimes])) * 1e3
     main_rows = int((x["state"][0] == -1).sum())
     n_drafted = int(t_nd.item())
+    del topk_ws
+
+    # Packed-tray verification for an autoregressive target (24 trays of 16
+    # drafted tokens, the packed budget of 384): causal tray attention over
+    # this workload's context and heads, then rejection sampling on seeded
+    # target logits and proposals of the same shape.
+    n_tr, B_tr = 24, 16
+    tr_logits, tr_q, tr_tok = synth.draw_trays(n_tr, B_tr, wl.V, seed=wl.seed + 500, T=1.0, drift=0.6)
+    tl, tq, tt = (torch.from_numpy(v).cuda() for v in (tr_logits, tr_q, tr_tok))
+    del tr_logits, tr_q
+    tr_na = torch.zeros(n_tr, dtype=torch.int32, device="cuda")
+    tr_nt = torch.zeros(n_tr, dtype=torch.int32, device="cuda")
+    rj_wsb = sfv.sfv_reject_workspace_bytes(n_tr, B_tr, wl.V)
+    rj_ws = torch.empty(rj_wsb, dtype=torch.uint8, device="cuda")
+    rng_t = np.random.default_rng(wl.seed + 501)
+    tq_bits = lambda *sh: torch.from_numpy(
+        synth.f32_to_bf16_bits(rng_t.standard_normal(sh, dtype=np.float32))).view(torch.bfloat16).cuda()
+    ta_q = tq_bits(n_tr, B_tr, wl.Hq, wl.d)
+    ta_k = tq_bits(n_tr, B_tr, wl.Hkv, wl.d)
+    ta_v = tq_bits(n_tr, B_tr, wl.Hkv, wl.d)
+    ta_o = torch.empty((n_tr, B_tr, wl.Hq, wl.d), dtype=torch.bfloat16, device="cuda")
+    ta_lse = torch.empty((n_tr, B_tr, wl.Hq), dtype=torch.float32, device="cuda")
+    ta_wsb = sfv.sfv_attend_workspace_bytes(n_tr, B_tr, wl.L, wl.Hq, wl.Hkv, wl.d)
+    ta_ws = torch.empty(max(ta_wsb, 16), dtype=torch.uint8, device="cuda")
+
+    def trays_once(ev=None):
+        sfv.sfv_attend_trays(ta_q, ta_k, ta_v, xd["k_ctx"], xd["v_ctx"], n_tr, B_tr, wl.L, wl.Hq, wl.Hkv, wl.d,
+                             1.0 / np.sqrt(wl.d), ta_o, ta_lse, ta_ws, ta_wsb)
+        if ev is not None:
+            ev.record(stream)
+        sfv.sfv_reject_verify(tl, tq, tt, n_tr, B_tr, wl.V, 1.0, wl.seed, wl.step0, wl.pos0, tr_na, tr_nt,
+                              rj_ws, rj_wsb)
+
+    for _ in range(2):
+        trays_once()
+    torch.cuda.synchronize()
+    ttimes = []
+    for s_ in range(a.steps):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        trays_once(e1)
+        e2.record(stream)
+        ttimes.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    tray_attn_us = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ttimes])) * 1e3
+    reject_us = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ttimes])) * 1e3
+    tray_accepted = tr_na.cpu().numpy()
+    reject_bytes = 2 * 4 * n_tr * (B_tr + 1) * wl.V + 4 * n_tr * wl.V * 2   # two passes per row + emitting rows
+    del tl, tq, tt, rj_ws, ta_q, ta_k, ta_v, ta_o, ta_lse, ta_ws
     ms_per_step = elapsed / a.steps * 1e3
     alg = algorithmic(wl, M)
     lm_bytes, lm_flop = alg["lm_head"]
@@ -314,6 +363,9 @@ def main():
     out["drafting"] = {"K": K_top, "D": D_tree, "W": W_tree, "topk_us": topk_us, "tree_us": tree_us,
                        "main_masked_rows": main_rows, "drafts_built": n_drafted,
                        "topk_hbm_frac": 2 * 4 * main_rows * wl.V / (topk_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    out["tray_verify"] = {"n_trays": n_tr, "B": B_tr, "temperature": 1.0, "attention_us": tray_attn_us,
+                          "reject_us": reject_us, "mean_accepted": float(tray_accepted.mean()),
+                          "reject_hbm_frac": reject_bytes / (reject_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
     out["commit_threshold"] = {"k_max": k_thr, "tau": tau_thr, "us": thr_us,
                                "positions_committed": thr_taken,
                                "hbm_frac": cb / (thr_us * 1e-6) / 1e9 / HBM_PEAK_GBS}

@@ -102,10 +102,14 @@ struct RejectPlan {
 struct RejectWs {
   float* row_max;    // [n][B+1] max of the (scaled) logits
   int* row_arg;      // [n][B+1] first index attaining it
-  double* row_sum;   // [n][B+1] sum exp(z - max), fp64
   int* accept;       // [n][B+1] drafted token accepted (positions < B)
+  double* chunk_sum; // [n][S] exact partial denominators of the emitting row
   double* chunk_key; // [n][S]
   int* chunk_id;     // [n][S]
+  float* chunk_max;  // [n][B+1][S] per-chunk max of z
+  int* chunk_arg;    // [n][B+1][S] its first index
+  double* chunk_sum_f;  // [n][B+1][S] fast sum of exp(z - chunk max)
+  double* chunk_err;    // [n][B+1][S] bound on its error
 };
 RejectPlan reject_plan(int n, int B, int V);
 hipError_t launch_reject(const float* logits, const float* q, const int32_t* tokens, int n, int B, int V,

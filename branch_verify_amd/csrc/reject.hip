@@ -6,15 +6,18 @@
 // the proposal probabilities, which keeps the target's distribution; trays
 // prepared for each plausible rejection point are served on a match.
 //
-// reject_stats_kernel: one workgroup per (tray, position) row of target
-// logits.  T > 0: z = fl32(l * invT), M = max z, S = sum exp(z - M) in fp64
-// (exact exp); at a drafted position the acceptance test u * q(x) < p(x)
-// with p(x) = exp(z_x - M) / S.  T = 0: the first argmax, and acceptance iff
-// the drafted token is it.
-// reject_sample_kernel: T > 0 only.  Each tray's emitting row (its first
-// rejection, else the bonus row) is cut into chunks; each chunk's best
-// Gumbel-max key over the residual ln(p - q) + g (or the bonus key z + g),
-// all in fp64.
+// reject_chunk_kernel + reject_accept_kernel: every (tray, position) row of
+// target logits is cut into chunks (one workgroup each: chunk max, first
+// argmax, fast exp sum with its bound), then one wave per row merges them.
+// T > 0: z = fl32(l * invT), M = max z; at a drafted position the acceptance
+// test u * q(x) < p(x), p(x) = exp(z_x - M) / S, is taken on the fast S with
+// its proven error bound, and on the exact fp64 S only when the bound
+// straddles the threshold.  T = 0: acceptance iff the drafted token is the
+// first argmax.
+// reject_emit_sum_kernel, reject_sample_kernel: T > 0 only.  Each tray's
+// emitting row (its first rejection, else the bonus row) is cut into chunks:
+// exact fp64 partial denominators, then each chunk's best Gumbel-max key
+// over the residual ln(p - q) + g (or the bonus key z + g), all in fp64.
 // reject_finalize_kernel: one wave per tray merges the chunks.
 // match_trays_kernel: one wave finds the lowest prepared tray matching.
 #include "common.h"
@@ -73,61 +76,177 @@ __device__ __forceinline__ void block_reduce_max_f(float& v, int& i, float* sv, 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void reject_stats_kernel(RejectArgs a) {
-  __shared__ float s_v[kThreads / kWave];
-  __shared__ int s_i[kThreads / kWave];
-  __shared__ double s_d[kThreads / kWave];
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  const int row = blockIdx.x;  // j * (B + 1) + pos
-  const int j = row / (a.B + 1), pos = row % (a.B + 1);
-  const float* l = a.logits + (size_t)row * a.V;
-
-  // max (T > 0: of fl32(l * invT)) with the first index attaining it
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  for (int v = t; v < a.V; v += kThreads) {
-    const float z = a.noisy ? l[v] * a.inv_t : l[v];
-    const bool take = (z > bv) | ((z == bv) & (v < bi));
-    bv = take ? z : bv;
-    bi = take ? v : bi;
-  }
-  block_reduce_max_f(bv, bi, s_v, s_i);
-  const float M = bv;
-  if (t == 0) {
-    a.ws.row_max[row] = M;
-    a.ws.row_arg[row] = bi;
-  }
-  if (!a.noisy) {
-    if (t == 0 && pos < a.B) a.ws.accept[row] = a.tokens[j * a.B + pos] == bi;
-    return;
-  }
-  double sum = 0.0;
-  for (int v = t; v < a.V; v += kThreads) sum += exp((double)(l[v] * a.inv_t) - (double)M);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-  if (lane == 0) s_d[wave] = sum;
-  __syncthreads();
-  if (t == 0) {
-    double S = 0.0;
-    for (int w = 0; w < kThreads / kWave; ++w) S += s_d[w];
-    a.ws.row_sum[row] = S;
-    if (pos < a.B) {
-      const int x = min(max(a.tokens[j * a.B + pos], 0), a.V - 1);  // tokens are in [0, V)
-      const double px = exp((double)(l[x] * a.inv_t) - (double)M) / S;
-      const unsigned w = noise_word(a.seed, a.step0 + (uint64_t)j, (uint64_t)(a.pos0 + pos), 0, kStreamAccept);
-      const double u = ((double)w + 0.5) * 2.3283064365386962890625e-10;
-      const double qx = (double)a.q[((size_t)j * a.B + pos) * a.V + x];
-      a.ws.accept[row] = u * qx < px;
-    }
-  }
-}
-
 // First rejected position of tray j (B if every drafted token passes).
 __device__ __forceinline__ int first_reject(const RejectArgs& a, int j) {
   int r = a.B;
   for (int t = a.B - 1; t >= 0; --t)
     if (!a.ws.accept[j * (a.B + 1) + t]) r = t;
   return r;
+}
+
+constexpr int kUnroll = 4;
+
+// Per (row, chunk): the chunk's max of z (T > 0: fl32(l * invT); T = 0: l)
+// with its first index, and (T > 0) the fast sum of exp(z - chunk max) with
+// its error bound.  Fast terms: d = fl32(z - m) and c = fl32(d * log2 e)
+// carry a relative exponent error below 3 * 2^-24 |c|; hardware exp2 is
+// within 2^-22 on [-126, 0] (certified by the self-check); terms flushed
+// below 2^-126 are covered by an absolute 2^-126 each.
+__global__ __launch_bounds__(kThreads) void reject_chunk_kernel(RejectArgs a) {
+  __shared__ float s_v[kThreads / kWave];
+  __shared__ int s_i[kThreads / kWave];
+  __shared__ double s_d[kThreads / kWave], s_e[kThreads / kWave];
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int row = blockIdx.x / a.S, sc = blockIdx.x % a.S;
+  const float* l = a.logits + (size_t)row * a.V;
+  const int c0 = sc * a.C, c1 = min(a.V, c0 + a.C);
+  const float scale = a.noisy ? a.inv_t : 1.f;
+
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int v0 = c0 + t; v0 < c1; v0 += kThreads * kUnroll) {
+    float x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = l[min(v0 + u * kThreads, c1 - 1)];  // loads unconditional
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kThreads;
+      const float z = x[u] * scale;
+      const bool take = (v < c1) & ((z > bv) | ((z == bv) & (v < bi)));
+      bv = take ? z : bv;
+      bi = take ? v : bi;
+    }
+  }
+  block_reduce_max_f(bv, bi, s_v, s_i);
+  const int slot = row * a.S + sc;
+  if (t == 0) {
+    a.ws.chunk_max[slot] = bv;
+    a.ws.chunk_arg[slot] = bi;
+  }
+  if (!a.noisy) return;
+  const float m = bv;
+  const float log2e = 1.4426950408889634f;
+  double sum = 0.0, err = 0.0;
+  for (int v0 = c0 + t; v0 < c1; v0 += kThreads * kUnroll) {
+    float x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = l[min(v0 + u * kThreads, c1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float c = (x[u] * a.inv_t - m) * log2e;
+      const double tv = v0 + u * kThreads < c1 ? (double)__builtin_amdgcn_exp2f(c) : 0.0;
+      sum += tv;
+      err += tv * (2.4e-7 + 1.8e-7 * (double)fabsf(c));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o, kWave);
+    err += __shfl_xor(err, o, kWave);
+  }
+  if (lane == 0) {
+    s_d[wave] = sum;
+    s_e[wave] = err;
+  }
+  __syncthreads();
+  if (t == 0) {
+    a.ws.chunk_sum_f[slot] = (s_d[0] + s_d[1]) + (s_d[2] + s_d[3]);
+    a.ws.chunk_err[slot] = (s_e[0] + s_e[1]) + (s_e[2] + s_e[3]);
+  }
+}
+
+// Per row: the row's max and first argmax from its chunks; at a drafted
+// position the acceptance test u * q(x) < exp(z_x - M) / S, on the fast S
+// (chunk sums rescaled to M by hardware exp2, bound carried) when the bound
+// decides it, else on the exact fp64 S.  One wave.
+__global__ __launch_bounds__(kWave) void reject_accept_kernel(RejectArgs a) {
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  const int j = row / (a.B + 1), pos = row % (a.B + 1);
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int c = lane; c < a.S; c += kWave) {
+    const float v = a.ws.chunk_max[row * a.S + c];
+    const int i = a.ws.chunk_arg[row * a.S + c];
+    const bool take = (v > bv) | ((v == bv) & (i < bi));
+    bv = take ? v : bv;
+    bi = take ? i : bi;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+    bv = take ? ov : bv;
+    bi = take ? oi : bi;
+  }
+  const float M = bv;
+  if (lane == 0) {
+    a.ws.row_max[row] = M;
+    a.ws.row_arg[row] = bi;
+  }
+  if (pos == a.B) return;  // the bonus row needs only its max and argmax
+  const int x = min(max(a.tokens[j * a.B + pos], 0), a.V - 1);  // tokens are in [0, V)
+  if (!a.noisy) {
+    if (lane == 0) a.ws.accept[row] = x == bi;
+    return;
+  }
+  const float log2e = 1.4426950408889634f;
+  double S = 0.0, E = 0.0;
+  for (int c = lane; c < a.S; c += kWave) {
+    const float arg = (a.ws.chunk_max[row * a.S + c] - M) * log2e;
+    const double r = (double)__builtin_amdgcn_exp2f(arg);
+    const double eps = 2.4e-7 + 1.8e-7 * (double)fabsf(arg);
+    const double sc = a.ws.chunk_sum_f[row * a.S + c];
+    S += sc * r;
+    E += (a.ws.chunk_err[row * a.S + c] + sc * eps) * r;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    S += __shfl_xor(S, o, kWave);
+    E += __shfl_xor(E, o, kWave);
+  }
+  E = E * 1.01 + (double)a.V * 1.2e-38 + S * 1e-10;
+  const float* l = a.logits + (size_t)row * a.V;
+  const double ex = exp((double)(l[x] * a.inv_t) - (double)M);
+  const unsigned w = noise_word(a.seed, a.step0 + (uint64_t)j, (uint64_t)(a.pos0 + pos), 0, kStreamAccept);
+  const double u = ((double)w + 0.5) * 2.3283064365386962890625e-10;
+  const double uq = u * (double)a.q[((size_t)j * a.B + pos) * a.V + x];
+  int acc;
+  if (uq * (S + E) < ex * (1.0 - 1e-15)) {
+    acc = 1;
+  } else if (uq * (S - E) > ex * (1.0 + 1e-15)) {
+    acc = 0;
+  } else {  // the bound straddles the threshold: the exact fp64 sum decides
+    double exact = 0.0;
+    for (int v = lane; v < a.V; v += kWave) exact += exp((double)(l[v] * a.inv_t) - (double)M);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) exact += __shfl_xor(exact, o, kWave);
+    acc = uq < ex / exact;
+  }
+  if (lane == 0) a.ws.accept[row] = acc;
+}
+
+// Exact fp64 softmax denominators of each tray's emitting row when it emits
+// from the residual: partial sums per chunk (summed in chunk order by the
+// sampler).
+__global__ __launch_bounds__(kThreads) void reject_emit_sum_kernel(RejectArgs a) {
+  __shared__ double s_d[kThreads / kWave];
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int j = blockIdx.x / a.S, sc = blockIdx.x % a.S;
+  const int r = first_reject(a, j);
+  if (r == a.B) return;
+  const int row = j * (a.B + 1) + r;
+  const float* l = a.logits + (size_t)row * a.V;
+  const float M = a.ws.row_max[row];
+  const int c0 = sc * a.C, c1 = min(a.V, c0 + a.C);
+  double sum = 0.0;
+  for (int v = c0 + t; v < c1; v += kThreads) sum += exp((double)(l[v] * a.inv_t) - (double)M);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+  if (lane == 0) s_d[wave] = sum;
+  __syncthreads();
+  if (t == 0) a.ws.chunk_sum[j * a.S + sc] = (s_d[0] + s_d[1]) + (s_d[2] + s_d[3]);
 }
 
 __global__ __launch_bounds__(kThreads) void reject_sample_kernel(RejectArgs a) {
@@ -141,7 +260,9 @@ __global__ __launch_bounds__(kThreads) void reject_sample_kernel(RejectArgs a) {
   const float* qr = a.q + ((size_t)j * a.B + min(r, a.B - 1)) * a.V;
   const bool residual = r < a.B;
   const float M = a.ws.row_max[row];
-  const double S = a.ws.row_sum[row];
+  double S = 0.0;
+  if (residual)
+    for (int c = 0; c < a.S; ++c) S += a.ws.chunk_sum[j * a.S + c];
   const uint64_t step = a.step0 + (uint64_t)j, posn = (uint64_t)(a.pos0 + r);
   const int c0 = sc * a.C, c1 = min(a.V, c0 + a.C);
   double bk = -INFINITY;
@@ -258,9 +379,10 @@ RejectPlan reject_plan(int n, int B, int V) {
   pl.S = S;
   pl.C = C;
   const size_t rows = (size_t)n * (B + 1);
-  pl.ws_bytes = align256(rows * sizeof(float)) + align256(rows * sizeof(int)) + align256(rows * sizeof(double)) +
-                align256(rows * sizeof(int)) + align256((size_t)n * S * sizeof(double)) +
-                align256((size_t)n * S * sizeof(int));
+  pl.ws_bytes = align256(rows * sizeof(float)) + align256(rows * sizeof(int)) + align256(rows * sizeof(int)) +
+                align256((size_t)n * S * sizeof(double)) + align256((size_t)n * S * sizeof(double)) +
+                align256((size_t)n * S * sizeof(int)) + align256(rows * S * sizeof(float)) +
+                align256(rows * S * sizeof(int)) + 2 * align256(rows * S * sizeof(double));
   return pl;
 }
 
@@ -272,13 +394,21 @@ RejectWs reject_ws(void* base, int n, int B, const RejectPlan& plan) {
   p += align256(rows * sizeof(float));
   ws.row_arg = (int*)p;
   p += align256(rows * sizeof(int));
-  ws.row_sum = (double*)p;
-  p += align256(rows * sizeof(double));
   ws.accept = (int*)p;
   p += align256(rows * sizeof(int));
+  ws.chunk_sum = (double*)p;
+  p += align256((size_t)n * plan.S * sizeof(double));
   ws.chunk_key = (double*)p;
   p += align256((size_t)n * plan.S * sizeof(double));
   ws.chunk_id = (int*)p;
+  p += align256((size_t)n * plan.S * sizeof(int));
+  ws.chunk_max = (float*)p;
+  p += align256(rows * plan.S * sizeof(float));
+  ws.chunk_arg = (int*)p;
+  p += align256(rows * plan.S * sizeof(int));
+  ws.chunk_sum_f = (double*)p;
+  p += align256(rows * plan.S * sizeof(double));
+  ws.chunk_err = (double*)p;
   return ws;
 }
 
@@ -302,10 +432,16 @@ hipError_t launch_reject(const float* logits, const float* q, const int32_t* tok
   a.ws = reject_ws(ws, n, B, plan);
   a.n_accept = n_accept;
   a.next_token = next_token;
-  hipLaunchKernelGGL(reject_stats_kernel, dim3(n * (B + 1)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(reject_chunk_kernel, dim3(n * (B + 1) * plan.S), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reject_accept_kernel, dim3(n * (B + 1)), dim3(kWave), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (a.noisy) {
+    hipLaunchKernelGGL(reject_emit_sum_kernel, dim3(n * plan.S), dim3(kThreads), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reject_sample_kernel, dim3(n * plan.S), dim3(kThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
