@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the attention in order on the main stream instead of beside the LM head")
+    ap.add_argument("--attn-with", choices=["commit", "lm_head"], default="lm_head",
+                    help="start the overlapped attention after the LM head (beside the commit) or with it")
     ap.add_argument("--no-graph", action="store_true",
                     help="issue the timed steps call by call instead of replaying a HIP graph")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -158,14 +160,14 @@ def main():
     # second stream, joined inside each step), replayed from a HIP graph of
     # one step unless --no-graph, bracketed by synchronize.
     if not a.no_graph:
-        step.capture(xd, overlap=not a.no_overlap)
+        step.capture(xd, overlap=not a.no_overlap, attn_with=a.attn_with)
         for _ in range(2):
             step.replay()
         torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(a.steps):
         if a.no_graph:
-            step.run(xd, overlap=not a.no_overlap)
+            step.run(xd, overlap=not a.no_overlap, attn_with=a.attn_with)
         else:
             step.replay()
     torch.cuda.synchronize()
@@ -343,7 +345,8 @@ def main():
                    "Hkv": wl.Hkv, "d": wl.d, "D": wl.D, "V": wl.V, "masked_rows": M,
                    "temperature": wl.T, "parallelism": "none (1 GPU)",
                    "launch": "call by call" if a.no_graph else "hip graph",
-                   "attention": "in order" if a.no_overlap else "beside the LM head"},
+                   "attention": "in order" if a.no_overlap else
+                   ("beside the commit" if a.attn_with == "commit" else "beside the LM head")},
         "roofline": {"bound": "hbm", "kernel": "lm_head", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,

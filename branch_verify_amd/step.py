@@ -84,13 +84,15 @@ class VerifyStep:
         sfv.sfv_match_tree(x["state"], self.next_state, self.commit_pos, self.parent, self.B1,
                            self.N, self.k_max, self.S_max, self.chain, self.n_accepted, self.status, stream)
 
-    def run(self, x, stream=None, overlap=True):
+    def run(self, x, stream=None, overlap=True, attn_with="lm_head"):
         """The whole hot path, stream-ordered, no host synchronisation.
 
-        Attention depends only on q/k/v, so with overlap=True it is issued on a
-        second stream after the LM head (which depends on the masked rows only)
-        and joined before the call returns; everything else stays in order on
-        `stream`."""
+        Attention depends only on q/k/v, so with overlap=True it runs on a
+        second stream, joined before the call returns; everything else stays
+        in order on `stream`.  attn_with="commit" starts it when the LM head
+        is done, beside the commit and the walk (the LM head keeps the whole
+        GPU); attn_with="lm_head" (the default, measured faster: the commit's
+        sweep also fills the GPU) starts it with the LM head."""
         if not overlap:
             self.attend(x, stream)
             self.masked_rows(x, stream)
@@ -103,17 +105,20 @@ class VerifyStep:
             self._side = torch.cuda.Stream(device=main.device)
             self._fork = torch.cuda.Event()
             self._join = torch.cuda.Event()
-        self._fork.record(main)
-        self._side.wait_event(self._fork)
+        if attn_with == "lm_head":
+            self._fork.record(main)
         self.masked_rows(x, main)
         self.lm_head(x, main)
+        if attn_with != "lm_head":
+            self._fork.record(main)
+        self._side.wait_event(self._fork)
         self.attend(x, self._side)
         self.commit(x, stream=main)
         self.match(x, main)
         self._join.record(self._side)
         main.wait_event(self._join)
 
-    def capture(self, x, overlap=True):
+    def capture(self, x, overlap=True, attn_with="lm_head"):
         """Capture one whole step (both streams) in a HIP graph; replay() then
         launches it with one call.  The graph holds the current buffers and
         inputs: replays recompute the same step."""
@@ -122,10 +127,10 @@ class VerifyStep:
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            self.run(x, stream=cap, overlap=overlap)  # warm the side stream and events outside capture
+            self.run(x, stream=cap, overlap=overlap, attn_with=attn_with)  # warm the side stream outside capture
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=cap):
-            self.run(x, stream=cap, overlap=overlap)
+            self.run(x, stream=cap, overlap=overlap, attn_with=attn_with)
         torch.cuda.synchronize()
         self._graph = g
         return g
