@@ -263,100 +263,129 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
   }
 
   // Logit loads are unconditional: a lane past the range end reads the last
-  // 8 ids of the range and then replaces the values by -inf, so the compiler
-  // never has to drain outstanding loads at a branch.  At T = 0 the next
-  // iteration's logits are loaded before this one's are used.
+  // 8 ids of the range and then drops them, so the compiler never has to
+  // drain outstanding loads at a branch.
   const float* rbase[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) rbase[k] = a.logits + (size_t)(k < nrows ? row[k] : row[0]) * a.V;
   const int vlast = ve - 8;  // ve - vb >= 8: both are multiples of 8
-  float4 pf0 = make_float4(0.f, 0.f, 0.f, 0.f), pf1 = pf0;
-  if (!NOISY) {
-    const int vc = min(vb + 8 * t, vlast);
-    pf0 = *(const float4*)(rbase[0] + vc);
-    pf1 = *(const float4*)(rbase[0] + vc + 4);
-  }
 
-  // The trip count is uniform across the workgroup (cross-lane reductions run
-  // inside the loop); a lane past the range end keeps every value at -inf.
-  for (int v0 = vb; v0 < ve; v0 += kPerIter) {
-    const int v = v0 + 8 * t;
-    const bool active = v < ve;  // ve and v are multiples of 8
-    const int vc = min(v, vlast);
-    float4 nf0 = pf0, nf1 = pf1;
-    if (!NOISY) {
-      const int vn = min(v + kPerIter, vlast);
-      nf0 = *(const float4*)(rbase[0] + vn);
-      nf1 = *(const float4*)(rbase[0] + vn + 4);
+  if constexpr (!NOISY) {
+    // Greedy sweep.  Two iterations' logits are in flight in two register
+    // sets used in turn (no register copies, which would make the compiler
+    // wait for the newest loads).  One max update per 8 ids; the 8 terms are
+    // summed in fp32 (at most 7 roundings of a sum of positive terms: below
+    // 2^-21 of it) and the group sum is added in fp64.
+    auto load8 = [&](float4& x0, float4& x1, int v) {
+      const int vc = min(v, vlast);
+      x0 = *(const float4*)(rbase[0] + vc);
+      x1 = *(const float4*)(rbase[0] + vc + 4);
+    };
+    auto take8 = [&](const float4& x0, const float4& x1, int v) {
+      if (v >= ve) return;  // ve and v are multiples of 8
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float m8 = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, x[e]);
+      if (m8 > lmax[0]) {
+        int e8 = 7;
+#pragma unroll
+        for (int e = 6; e >= 0; --e) e8 = x[e] == m8 ? e : e8;
+        if (lmax[0] != -INFINITY) {
+          const float af = m8 - lmax[0];
+          const float f = fast_exp2(-af * kLog2e);
+          S[0] *= (double)f;
+          E[0] = E[0] * f + (float)S[0] * (kC1 * af + kC2);
+        }
+        lmax[0] = m8;
+        lidx[0] = v + e8;
+      }
+      float gs = 0.f, ga = 0.f;  // sum of terms, sum of term * argument
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float am = lmax[0] - x[e];
+        const float tt = fast_exp2(-am * kLog2e);
+        gs += tt;
+        ga += tt * am;
+      }
+      S[0] += (double)gs;
+      E[0] += kC1 * ga + (kC2 + 4.76837158e-7f) * gs;
+    };
+    float4 a0, a1, b0, b1;
+    load8(a0, a1, vb + 8 * t);
+    load8(b0, b1, vb + kPerIter + 8 * t);
+    for (int v0 = vb; v0 < ve; v0 += 2 * kPerIter) {
+      const int v = v0 + 8 * t;
+      take8(a0, a1, v);
+      load8(a0, a1, v + 2 * kPerIter);
+      take8(b0, b1, v + kPerIter);
+      load8(b0, b1, v + 3 * kPerIter);
     }
-    unsigned wd[8];
-    float gf[8];
-    if (NOISY) {
+  } else {
+    // The trip count is uniform across the workgroup (cross-lane reductions
+    // run inside the loop); a lane past the range end keeps every value at
+    // -inf.
+    for (int v0 = vb; v0 < ve; v0 += kPerIter) {
+      const int v = v0 + 8 * t;
+      const bool active = v < ve;  // ve and v are multiples of 8
+      const int vc = min(v, vlast);
+      unsigned wd[8];
+      float gf[8];
       noise_block(a.seed, step, pos, (uint64_t)(v >> 3), wd);
 #pragma unroll
       for (int e = 0; e < 8; ++e) gf[e] = gumbel_fast(wd[e]);
-    }
-    // (predicated blocks, not breaks, so that every loop unrolls and the small
-    // arrays stay in registers)
+      // (predicated blocks, not breaks, so that every loop unrolls and the
+      // small arrays stay in registers)
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      if (k < nrows) {
-      float4 x0, x1;
-      if (!NOISY) {
-        x0 = pf0;
-        x1 = pf1;
-      } else {
-        x0 = *(const float4*)(rbase[k] + vc);
-        x1 = *(const float4*)(rbase[k] + vc + 4);
-      }
-      // (an inactive lane's values are never used: the sums below are guarded
-      // and its Gumbel keys are -inf)
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      // running max / first argmax and the confidence sum (this lane's ids)
-      if (active) {
+      for (int k = 0; k < R; ++k) {
+        if (k < nrows) {
+          const float4 x0 = *(const float4*)(rbase[k] + vc);
+          const float4 x1 = *(const float4*)(rbase[k] + vc + 4);
+          // (an inactive lane's values are never used: the sums below are
+          // guarded and its Gumbel keys are -inf)
+          const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          // running max / first argmax and the confidence sum (this lane's ids)
+          if (active) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float xe = x[e];
-          if (xe > lmax[k]) {
-            if (lmax[k] != -INFINITY) {
-              const float af = xe - lmax[k];
-              const float f = fast_exp2(-af * kLog2e);
-              S[k] *= (double)f;
-              E[k] = E[k] * f + (float)S[k] * (kC1 * af + kC2);
+            for (int e = 0; e < 8; ++e) {
+              const float xe = x[e];
+              if (xe > lmax[k]) {
+                if (lmax[k] != -INFINITY) {
+                  const float af = xe - lmax[k];
+                  const float f = fast_exp2(-af * kLog2e);
+                  S[k] *= (double)f;
+                  E[k] = E[k] * f + (float)S[k] * (kC1 * af + kC2);
+                }
+                lmax[k] = xe;
+                lidx[k] = v + e;
+              }
+              const float am = lmax[k] - xe;
+              const float tt = fast_exp2(-am * kLog2e);
+              S[k] += (double)tt;
+              E[k] += tt * (kC1 * am + kC2);
             }
-            lmax[k] = xe;
-            lidx[k] = v + e;
           }
-          const float am = lmax[k] - xe;
-          const float tt = fast_exp2(-am * kLog2e);
-          S[k] += (double)tt;
-          E[k] += tt * (kC1 * am + kC2);
-        }
-      }
-      if (NOISY) {
-        float ka[8], lm = -INFINITY;
+          float ka[8], lm = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ka[e] = active ? (x[e] * a.inv_t) + gf[e] : -INFINITY;
-          lm = fmaxf(lm, ka[e]);
-        }
-        wbest[k] = fmaxf(wbest[k], wave_max(lm));
-        const float thr = wbest[k] - (2.f * kGumbelEps + 4.f * 1.1920929e-7f * fabsf(wbest[k]) + 1e-30f);
+          for (int e = 0; e < 8; ++e) {
+            ka[e] = active ? (x[e] * a.inv_t) + gf[e] : -INFINITY;
+            lm = fmaxf(lm, ka[e]);
+          }
+          wbest[k] = fmaxf(wbest[k], wave_max(lm));
+          const float thr = wbest[k] - (2.f * kGumbelEps + 4.f * 1.1920929e-7f * fabsf(wbest[k]) + 1e-30f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (active && ka[e] >= thr) {
-            const float key = (x[e] * a.inv_t) + gumbel_exact(wd[e]);
-            if (key > kmax[k]) {
-              kmax[k] = key;
-              kidx[k] = v + e;
+          for (int e = 0; e < 8; ++e) {
+            if (active && ka[e] >= thr) {
+              const float key = (x[e] * a.inv_t) + gumbel_exact(wd[e]);
+              if (key > kmax[k]) {
+                kmax[k] = key;
+                kidx[k] = v + e;
+              }
             }
           }
         }
       }
-      }
     }
-    pf0 = nf0;
-    pf1 = nf1;
   }
 
   // ---- reduce over the workgroup, row by row ----
