@@ -11,8 +11,9 @@ replayed from a HIP graph of one step, in which the attention (independent of
 the rest) runs on a second stream.  A
 second pass of K steps issued in order on one stream times each call with HIP
 events on the stream it runs on; the roofline object reports the dominant
-kernel (the LM head) from those against the HBM peak, with the HBM traffic
-its byte counters measured.  cpu_baseline times the CPU oracle on this host.
+kernel (the LM head) from those against its binding peak (HBM bytes, or bf16
+MFMA FLOP when those take longer), with the HBM traffic its byte counters
+measured on this workload.  cpu_baseline times the CPU oracle on this host.
 """
 from __future__ import annotations
 
@@ -81,15 +82,17 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per LM-head launch from the committed counter summary, or None
-    when the kernel source changed since the counters were taken."""
+    when the counters were taken on another workload or the kernel source
+    changed since."""
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     text = open(PROFILE_TRAFFIC).read()
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     s = re.search(r"lm_head_source_sha256_16:\s*([0-9a-f]+)", text)
-    if not m or not s:
+    w = re.search(r"traffic_workload:\s*(\S+)", text)
+    if not m or not s or not w or w.group(1) != workload:
         return None
     here = source_digest(LM_HEAD_SOURCES)
     return float(m.group(1)) if s.group(1) == here else None
@@ -326,8 +329,11 @@ def main():
     alg = algorithmic(wl, M)
     lm_bytes, lm_flop = alg["lm_head"]
     lm_s = per["lm_head"] * 1e-6
-    achieved = lm_bytes / lm_s / 1e9
-    traffic = measured_traffic()
+    # the LM head's binding roofline: HBM bytes or bf16 MFMA FLOP, whichever
+    # takes longer at its peak
+    mfma_bound = lm_flop / (BF16_PEAK_TFLOPS * 1e12) > lm_bytes / (HBM_PEAK_GBS * 1e9)
+    achieved = lm_flop / lm_s / 1e12 if mfma_bound else lm_bytes / lm_s / 1e9
+    traffic = measured_traffic(wl.name)
     out = {
         "metric": METRIC,
         "value": wl.B1 * wl.N / (elapsed / a.steps),
@@ -347,9 +353,13 @@ def main():
                    "launch": "call by call" if a.no_graph else "hip graph",
                    "attention": "in order" if a.no_overlap else
                    ("beside the commit" if a.attn_with == "commit" else "beside the LM head")},
-        "roofline": {"bound": "hbm", "kernel": "lm_head", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "lm_head",
+                     "achieved": achieved,
+                     "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+                     "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                     "frac": achieved / (BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS),
                      "traffic": traffic,
+                     "hbm_frac": lm_bytes / lm_s / 1e9 / HBM_PEAK_GBS,
                      "mfma_frac": lm_flop / lm_s / 1e12 / BF16_PEAK_TFLOPS},
         "kernels_us": per,
         "ms_per_step_sequential": elapsed_seq / a.steps * 1e3,
