@@ -371,6 +371,73 @@ int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* s
                     "sfv_commit");
 }
 
+int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes) {
+  if (!bytes) return fail(SFV_E_INVAL, "bytes is NULL");
+  if (M < 0 || V < 1 || D < 1) return fail(SFV_E_INVAL, "M=%d, V=%d, D=%d out of range", M, V, D);
+  const int ns = sfv::lm_head_greedy_parts(M, V, D);
+  if (ns == 0) {
+    return fail(SFV_E_UNSUPPORTED, "greedy partials need 129 <= M <= 256, D %% 64 == 0 and D >= 128 (M=%d, D=%d)",
+                M, D);
+  }
+  *bytes = (size_t)ns * M * sizeof(sfv::GreedyPart);
+  return ok();
+}
+
+int sfv_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w, int D, int V,
+                       float* logits, void* partials, size_t partials_bytes, void* stream) {
+  size_t need = 0;
+  int rc = sfv_lm_head_greedy_bytes(M, V, D, &need);
+  if (rc != SFV_OK) return rc;
+  if (R < 1) return fail(SFV_E_INVAL, "R=%d < 1", R);
+  if ((double)M * V >= 9.0e15 || (double)V * D >= 9.0e15) return fail(SFV_E_INVAL, "too large");
+  if (!hidden || !rows || !w || !logits || !partials) return fail(SFV_E_INVAL, "null pointer");
+  const uintptr_t al = (uintptr_t)hidden | (uintptr_t)w | (uintptr_t)logits | (uintptr_t)partials;
+  if (al % 16 != 0) return fail(SFV_E_INVAL, "tensor pointers must be 16-byte aligned");
+  if (partials_bytes < need) return fail(SFV_E_WORKSPACE, "partials %zu bytes < %zu needed", partials_bytes, need);
+  return hip_status(sfv::launch_lm_head_greedy(hidden, rows, M, R, w, D, V, logits,
+                                               (sfv::GreedyPart*)partials, (hipStream_t)stream),
+                    "sfv_lm_head_greedy");
+}
+
+int sfv_commit_greedy_workspace_bytes(int B1, int N, int M, int V, size_t* bytes) {
+  if (!bytes) return fail(SFV_E_INVAL, "bytes is NULL");
+  const int rc = check_commit_dims(B1, N, M, V);
+  if (rc != SFV_OK) return rc;
+  *bytes = sfv::commit_greedy_ws_bytes(B1, N, M);
+  return ok();
+}
+
+int sfv_commit_greedy(const void* partials, size_t partials_bytes, int D, const float* logits,
+                      const int32_t* rows, int M, const int32_t* state, const int32_t* parent_host, int B1,
+                      int N, int V, int k_max, float tau, int32_t* next_state, int32_t* commit_pos,
+                      int32_t* token, float* conf, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_commit_dims(B1, N, M, V);
+  if (rc != SFV_OK) return rc;
+  size_t need_parts = 0;
+  rc = sfv_lm_head_greedy_bytes(M, V, D, &need_parts);
+  if (rc != SFV_OK) return rc;
+  if (!state || !next_state || !commit_pos || !workspace || !partials) return fail(SFV_E_INVAL, "null pointer");
+  if (!logits || !rows || !token || !conf) return fail(SFV_E_INVAL, "null pointer");
+  if (((uintptr_t)partials | (uintptr_t)logits) % 16 != 0) {
+    return fail(SFV_E_INVAL, "partials and logits must be 16-byte aligned");
+  }
+  if (partials_bytes < need_parts) {
+    return fail(SFV_E_WORKSPACE, "partials %zu bytes < %zu needed", partials_bytes, need_parts);
+  }
+  if (k_max < 1) return fail(SFV_E_INVAL, "k_max=%d < 1", k_max);
+  if (k_max > N) return fail(SFV_E_INVAL, "k_max=%d > N=%d", k_max, N);
+  if (k_max > 1 && !std::isfinite(tau)) return fail(SFV_E_INVAL, "tau must be finite");
+  sfv::TreeArgs tree;
+  rc = make_tree(parent_host, B1, &tree);
+  if (rc != SFV_OK) return rc;
+  const size_t need = sfv::commit_greedy_ws_bytes(B1, N, M);
+  if (workspace_bytes < need) return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  return hip_status(sfv::launch_commit_greedy((const sfv::GreedyPart*)partials, sfv::lm_head_greedy_parts(M, V, D),
+                                              logits, rows, M, state, tree, N, V, k_max, tau, next_state,
+                                              commit_pos, token, conf, workspace, (hipStream_t)stream),
+                    "sfv_commit_greedy");
+}
+
 int sfv_match_tree(const int32_t* state, const int32_t* next_state, const int32_t* commit_pos,
                    const int32_t* parent_host, int B1, int N, int k_max, int S_max, int32_t* chain,
                    int32_t* n_accepted, int32_t* status, void* stream) {

@@ -31,14 +31,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerIter = 8 * kThreads;  // vocab ids per workgroup iteration
 constexpr int kItemRows = 8;            // rows sharing one noise sweep
-constexpr float kLog2e = 1.44269504088896341f;
-
-// Error model of one fast term t = exp2(fl32(fl32(x - m) * log2e)), relative
-// to exp(x - m), for a = m - x >= 0:  |t / exp(x - m) - 1| <= kC1 * a + kC2.
-// kC1 covers the two fp32 roundings of the argument, kC2 the hardware exp2
-// (certified below 2^-22 by the self-check; 2^-20 is used).
-constexpr float kC1 = 3.5f / 16777216.0f;
-constexpr float kC2 = 1.0f / 1048576.0f;
+constexpr float kLog2e = kLog2eF;
+// error model of one fast term (internal.h): |t / exp(x - m) - 1| <= kC1 * a + kC2
+constexpr float kC1 = kExpC1;
+constexpr float kC2 = kExpC2;
 // Bound on |g_fast - g_exact| (certified below 1e-5 by the self-check).
 constexpr float kGumbelEps = 1.0f / 4096.0f;
 
@@ -720,6 +716,122 @@ __global__ __launch_bounds__(kThreads) void commit_finalize_kernel(FinArgs a, Ws
 }
 
 // ---------------------------------------------------------------------------
+// greedy commit from the fused LM head's tile partials
+// ---------------------------------------------------------------------------
+// Workgroup (row group g, chunk c): rows 4 g .. 4 g + 3 and the partials of
+// chunk c (one per vocab tile).  Thread t takes row 4 g + t % 4 and every
+// 64th partial from t / 4 (the four rows of a tile are 64 contiguous bytes;
+// a thread's loads are issued before the merging starts) into a running
+// (max, first argmax, S, E) with the sweep's error model: a partial's S is
+// rescaled by a fast factor when the running max moves or lies above the
+// partial's.  The 64 threads of a row then merge by shuffles with fast
+// factors of the same model and across the four waves in fp64, and the row's
+// partial for chunk c is written in the layout the finalize kernel reads.
+struct Run {
+  float m;
+  int i;
+  double S;
+  float E;
+};
+
+// Adds the partial (m2, i2, S2, E2) to r (fast factors, bounded).
+__device__ __forceinline__ void run_add(Run& r, float m2, int i2, double S2, float E2) {
+  if (m2 == -INFINITY) return;
+  if (m2 > r.m) {
+    if (r.m != -INFINITY) {
+      const float a = m2 - r.m;
+      const float f = fast_exp2(-a * kLog2e);
+      r.S *= (double)f;
+      r.E = r.E * f + (float)r.S * (kC1 * a + kC2);
+    }
+    r.m = m2;
+    r.i = i2;
+  } else if (m2 == r.m && i2 < r.i) {
+    r.i = i2;
+  }
+  const float a = r.m - m2;
+  const float f = fast_exp2(-a * kLog2e);
+  const double sf = S2 * (double)f;
+  r.S += sf;
+  r.E += E2 * f + (float)sf * (kC1 * a + kC2);
+}
+
+constexpr int kMergeRows = 4;                       // rows per workgroup
+constexpr int kMergeLanes = kThreads / kMergeRows;  // partial lanes per row
+constexpr int kMergeUnroll = 10;                    // loads in flight per thread
+
+__global__ __launch_bounds__(kThreads) void greedy_merge_kernel(const GreedyPart* gp, int nparts, int M,
+                                                                WsLayout ws) {
+  __shared__ float wm[kThreads / kWave][kMergeRows];
+  __shared__ int wi[kThreads / kWave][kMergeRows];
+  __shared__ double wsum[kThreads / kWave][kMergeRows];
+  __shared__ float we[kThreads / kWave][kMergeRows];
+  const int g = blockIdx.x / kGreedyChunks;
+  const int c = blockIdx.x % kGreedyChunks;
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int rr = t % kMergeRows, j = t / kMergeRows;
+  const int m = g * kMergeRows + rr;
+  const int mm = min(m, M - 1);  // pad rows read row M - 1 (in bounds) and are never written
+  const int per = (nparts + kGreedyChunks - 1) / kGreedyChunks;
+  const int s0 = c * per, s1 = min(nparts, s0 + per);
+  Run r{-INFINITY, 0x7FFFFFFF, 0.0, 0.f};
+  for (int sb = s0; sb < s1; sb += kMergeLanes * kMergeUnroll) {
+    GreedyPart e[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int st = min(sb + u * kMergeLanes + j, nparts - 1);
+      e[u] = gp[(size_t)st * M + mm];
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u)
+      if (sb + u * kMergeLanes + j < s1) {
+        // (a partial's S is an fp32 sum; 2^-23 of it covers one more rounding)
+        run_add(r, e[u].m, e[u].idx, (double)e[u].S, e[u].E + e[u].S * 1.1920929e-7f);
+      }
+  }
+#pragma unroll
+  for (int o = kMergeRows; o < kWave; o <<= 1) {  // lanes of the same row
+    const float m2 = __shfl_xor(r.m, o, kWave);
+    const int i2 = __shfl_xor(r.i, o, kWave);
+    const double S2 = __shfl_xor(r.S, o, kWave);
+    const float E2 = __shfl_xor(r.E, o, kWave);
+    run_add(r, m2, i2, S2, E2);
+  }
+  if (lane < kMergeRows) {
+    wm[wave][rr] = r.m;
+    wi[wave][rr] = r.i;
+    wsum[wave][rr] = r.S;
+    we[wave][rr] = r.E;
+  }
+  __syncthreads();
+  if (t < kMergeRows && m < M) {
+    float bm = wm[0][t];
+    int bi = wi[0][t];
+    for (int w = 1; w < kThreads / kWave; ++w)
+      if (better(wm[w][t], wi[w][t], bm, bi)) {
+        bm = wm[w][t];
+        bi = wi[w][t];
+      }
+    double tot = 0.0, err = 0.0;
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      if (wm[w][t] == -INFINITY) continue;
+      const double f = exp((double)wm[w][t] - (double)bm);  // fp64: exact to ~1 ulp
+      tot += wsum[w][t] * f;
+      err += (double)we[w][t] * f;
+    }
+    Partial pr;
+    pr.lmax = bm;
+    pr.lidx = bi;
+    pr.kmax = -INFINITY;
+    pr.kidx = 0x7FFFFFFF;
+    pr.S = tot;
+    pr.E = (float)(err * 1.0001 + tot * 1e-13);
+    pr.pad = 0;
+    ws.part[(size_t)m * kGreedyChunks + c] = pr;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // self-check of the fast-path bounds
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void atomic_max_pos_double(double* addr, double v) {
@@ -835,6 +947,38 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
   fa.k_max = k_max;
   fa.tau = tau;
   fa.noisy = noisy;
+  hipLaunchKernelGGL(commit_finalize_kernel, dim3(tree.B1), dim3(kThreads), 0, stream, fa, ws);
+  return hipGetLastError();
+}
+
+size_t commit_greedy_ws_bytes(int B1, int N, int M) { return ws_bytes(B1, N, M, 0, kGreedyChunks); }
+
+hipError_t launch_commit_greedy(const GreedyPart* gpart, int nparts, const float* logits,
+                                const int32_t* rows, int M, const int32_t* state, const TreeArgs& tree,
+                                int N, int V, int k_max, float tau, int32_t* next_state, int32_t* commit_pos,
+                                int32_t* token, float* conf, void* ws_base, hipStream_t stream) {
+  WsLayout ws = ws_layout(ws_base, tree.B1, N, M, 0);
+  if (M > 0) {
+    const unsigned blocks = (unsigned)((M + kMergeRows - 1) / kMergeRows) * kGreedyChunks;
+    hipLaunchKernelGGL(greedy_merge_kernel, dim3(blocks), dim3(kThreads), 0, stream, gpart, nparts, M, ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  FinArgs fa;
+  fa.logits = logits;
+  fa.rows = rows;
+  fa.M = M;
+  fa.state = state;
+  fa.next_state = next_state;
+  fa.commit_pos = commit_pos;
+  fa.token = token;
+  fa.conf = conf;
+  fa.N = N;
+  fa.V = V;
+  fa.splits = kGreedyChunks;
+  fa.k_max = k_max;
+  fa.tau = tau;
+  fa.noisy = false;
   hipLaunchKernelGGL(commit_finalize_kernel, dim3(tree.B1), dim3(kThreads), 0, stream, fa, ws);
   return hipGetLastError();
 }

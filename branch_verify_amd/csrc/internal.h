@@ -37,6 +37,32 @@ hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows
 hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R, const void* w,
                           int D, int V, float* logits, hipStream_t stream);
 
+// Error model of a fast confidence term t = exp2(fl32(fl32(x - m) * log2e))
+// against exp(x - m), for a = m - x >= 0:  |t / exp(x - m) - 1| <= kExpC1 * a +
+// kExpC2.  kExpC1 covers the two fp32 roundings of the argument, kExpC2 the
+// hardware exp2 (certified below 2^-22 by sfv_selfcheck_bounds; 2^-20 is used).
+constexpr float kLog2eF = 1.44269504088896341f;
+constexpr float kExpC1 = 3.5f / 16777216.0f;
+constexpr float kExpC2 = 1.0f / 1048576.0f;
+
+// Greedy partial of one row over a range of vocabulary ids (a 128-id vocab
+// tile when written by the fused LM head): the max logit, the lowest id
+// attaining it, the fp32 sum of exp(l - max) over the range and a bound on
+// that sum's error.
+struct GreedyPart {
+  float m;
+  int idx;
+  float S;
+  float E;
+};
+
+// Fused LM head + greedy partials: served for these shapes when the result
+// is > 0 (the number of partials per row, one per vocab tile; `gpart` is
+// [tiles][M]), else 0.
+int lm_head_greedy_parts(int M, int V, int D);
+hipError_t launch_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w,
+                                 int D, int V, float* logits, GreedyPart* gpart, hipStream_t stream);
+
 constexpr int kMaxBranches = 64;
 constexpr int kMaxBlock = 256;
 
@@ -67,6 +93,16 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
                          int32_t* commit_pos,
                          int32_t* token, float* conf, void* ws, const CommitPlan& plan,
                          hipStream_t stream);
+
+// Greedy commit from the fused LM head's tile partials: a merge kernel
+// reduces the partials of every row to kGreedyChunks, then the commit's
+// finalize kernel (the same one the vocabulary sweep feeds) decides.
+constexpr int kGreedyChunks = 2;
+size_t commit_greedy_ws_bytes(int B1, int N, int M);
+hipError_t launch_commit_greedy(const GreedyPart* gpart, int nparts, const float* logits,
+                                const int32_t* rows, int M, const int32_t* state, const TreeArgs& tree,
+                                int N, int V, int k_max, float tau, int32_t* next_state, int32_t* commit_pos,
+                                int32_t* token, float* conf, void* ws, hipStream_t stream);
 
 hipError_t launch_match(const int32_t* state, const int32_t* next_state, const int32_t* commit_pos,
                         const TreeArgs& tree, int N, int k_max, int S_max, int32_t* chain,

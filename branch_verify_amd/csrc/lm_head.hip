@@ -53,7 +53,8 @@ struct Params {
   const unsigned short* w;
   float* logits;
   int M, D, V, R;
-  int vt, mt;  // tile counts
+  int vt, mt;          // tile counts
+  GreedyPart* gpart;   // weight-streaming kernel only: tile partials [vocab tiles][M], or null
 };
 
 __global__ __launch_bounds__(kThreads) void lm_head_tiled(Params p) {
@@ -180,6 +181,97 @@ __global__ __launch_bounds__(kThreads) void lm_head_tiled(Params p) {
 // per workgroup differ by at most one.  With OCC = 1 the LDS is padded so that
 // no second workgroup fits a CU; with OCC = 2 two workgroups share each CU, so
 // one's LDS and barrier waits overlap the other's MFMAs.
+// Greedy partial of one row over a 32-id strip held by a lane pair: this
+// lane's 16 values are ids v0 + 8 q + j (q, j < 4; the partner lane, 32
+// away, holds v0 + 4 + 8 q + j).  Ids at or past V are left out.  Both lanes
+// return the strip's partial:
+//  * max and the lowest id attaining it (the lane's ids ascend, and the pair
+//    breaks a tie of maxima toward the lower id);
+//  * S = sum of fast terms exp2((x - max) log2e) in fp32 and E, a bound on
+//    |S - sum exp(x - max)|: each term within kExpC1 a + kExpC2 of its value
+//    (a = max - x), at most 15 roundings of a positive fp32 sum (below
+//    2^-20 of it) per lane, and the pair's rescale by fast factors of the same
+//    model plus 2 roundings (2^-22).
+__device__ __forceinline__ GreedyPart strip_partial(const floatx16& x, int v0, int V) {
+  float mx = -INFINITY;
+  int ix = 0x7FFFFFFF;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = v0 + 8 * q + j;
+      const float xv = v < V ? x[4 * q + j] : -INFINITY;
+      if (xv > mx) {
+        mx = xv;
+        ix = v;
+      }
+    }
+  float S = 0.f, A = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = v0 + 8 * q + j;
+        const float am = mx - x[4 * q + j];
+        const float tt = v < V ? __builtin_amdgcn_exp2f(-am * kLog2eF) : 0.f;
+        S += tt;
+        A += tt * am;
+      }
+  }
+  float E = kExpC1 * A + (kExpC2 + 9.5367431640625e-07f) * S;
+  const float mo = __shfl_xor(mx, 32, kWave);
+  const int io = __shfl_xor(ix, 32, kWave);
+  const float So = __shfl_xor(S, 32, kWave);
+  const float Eo = __shfl_xor(E, 32, kWave);
+  GreedyPart g;
+  g.m = fmaxf(mx, mo);
+  g.idx = (mo > mx || (mo == mx && io < ix)) ? io : ix;
+  if (g.m == -INFINITY) {
+    g.S = 0.f;
+    g.E = 0.f;
+    return g;
+  }
+  float s2 = 0.f, e2 = 0.f;
+  if (mx != -INFINITY) {
+    const float a = g.m - mx;
+    const float f = __builtin_amdgcn_exp2f(-a * kLog2eF);
+    s2 += S * f;
+    e2 += E * f + S * f * (kExpC1 * a + kExpC2);
+  }
+  if (mo != -INFINITY) {
+    const float a = g.m - mo;
+    const float f = __builtin_amdgcn_exp2f(-a * kLog2eF);
+    s2 += So * f;
+    e2 += Eo * f + So * f * (kExpC1 * a + kExpC2);
+  }
+  g.S = s2;
+  g.E = e2 + s2 * 2.384185791015625e-07f;
+  return g;
+}
+
+// r += e for two greedy partials of one row over disjoint id ranges, e's ids
+// above r's: the max, the lowest id attaining it, and the rescaled sum with
+// its bound (fast factors of the same model, 3 roundings: 2^-22).
+__device__ __forceinline__ void part_add(GreedyPart& r, const GreedyPart& e) {
+  if (e.m == -INFINITY) return;
+  if (r.m == -INFINITY) {
+    r = e;
+    return;
+  }
+  const float mx = fmaxf(r.m, e.m);
+  const int idx = e.m > r.m ? e.idx : r.idx;  // a tie keeps r's (lower) id
+  const float a1 = mx - r.m, a2 = mx - e.m;
+  const float f1 = __builtin_amdgcn_exp2f(-a1 * kLog2eF);
+  const float f2 = __builtin_amdgcn_exp2f(-a2 * kLog2eF);
+  const float s = r.S * f1 + e.S * f2;
+  r.E = r.E * f1 + e.E * f2 + r.S * f1 * (kExpC1 * a1 + kExpC2) + e.S * f2 * (kExpC1 * a2 + kExpC2) +
+        s * 2.384185791015625e-07f;
+  r.S = s;
+  r.m = mx;
+  r.idx = idx;
+}
+
 template <int MB, int VW, int P, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void lm_head_stream(Params p) {
   constexpr int MP = MB * 32;
@@ -189,6 +281,7 @@ __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(O
   constexpr int LDH = SK + 8;
   constexpr int TV = 128 * VW;  // vocab ids per tile
   __shared__ unsigned short hs[2][MPA][LDH];
+  __shared__ GreedyPart gx[4 * VW][MP];  // greedy partials of a tile's strips (when p.gpart)
 
   const int t = threadIdx.x;
   const int lane = t % kWave;
@@ -309,11 +402,28 @@ __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(O
               }
             }
           }
+          if (p.gpart) {  // (uniform) greedy partials of this row's 32-id strips, to LDS
+#pragma unroll
+            for (int b = 0; b < VW; ++b) {
+              const int strip = tile * 4 * VW + wave * VW + b;
+              const GreedyPart gp = strip_partial(acc[b][mb], strip * 32 + 4 * half, p.V);
+              if (half == 0) gx[wave * VW + b][m] = gp;
+            }
+          }
 #pragma unroll
           for (int b = 0; b < VW; ++b) acc[b][mb] = floatx16{};
         }
       }
       __syncthreads();
+      if (p.gpart && g % ksteps == ksteps - 1 && t < p.M) {
+        // the tile's partial of row t: its strips in id order (gx is next
+        // written a whole tile later, after as many barriers)
+        GreedyPart r = gx[0][t];
+#pragma unroll
+        for (int k = 1; k < 4 * VW; ++k) part_add(r, gx[k][t]);
+        const int tile = (int)blockIdx.x + (g / ksteps) * (int)gridDim.x;
+        p.gpart[(size_t)tile * p.M + t] = r;
+      }
     }
   }
 }
@@ -523,11 +633,39 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   p.R = R;
   p.vt = (V + BV - 1) / BV;
   p.mt = (M + BM - 1) / BM;
+  p.gpart = nullptr;
   // Up to 128 rows (one row tile): the tiled kernel.  129..256 rows: stream
   // the weight once past every row.  More rows: the large-tile kernel.
   if (M <= BM) return launch_tiled(p, stream);
   if (M <= kStreamRows) return launch_stream_rows(p, stream);
   return launch_big8(p, stream);
+}
+
+// The weight-streaming kernel (129..256 rows, one-wide vocab tiles of 128
+// ids) writes one greedy partial per row and vocab tile beside the logits.
+int lm_head_greedy_parts(int M, int V, int D) {
+  // (two or more k-stages per tile: a barrier separates the reads of a tile's
+  // strip partials from the next tile's writes)
+  if (M <= BM || M > kStreamRows || D % 64 != 0 || D < 128 || V < 1) return 0;
+  return (V + 127) / 128;
+}
+
+hipError_t launch_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w,
+                                 int D, int V, float* logits, GreedyPart* gpart, hipStream_t stream) {
+  if (lm_head_greedy_parts(M, V, D) == 0 || gpart == nullptr) return hipErrorInvalidValue;
+  Params p;
+  p.hidden = (const unsigned short*)hidden;
+  p.rows = rows;
+  p.w = (const unsigned short*)w;
+  p.logits = logits;
+  p.M = M;
+  p.D = D;
+  p.V = V;
+  p.R = R;
+  p.vt = (V + BV - 1) / BV;
+  p.mt = (M + BM - 1) / BM;
+  p.gpart = gpart;
+  return launch_stream_rows(p, stream);
 }
 
 }  // namespace sfv

@@ -25,6 +25,8 @@ EXPORTS = [
     "sfv_match_tree", "sfv_selfcheck_bounds", "sfv_fold_gate", "sfv_attend_folded_workspace_bytes",
     "sfv_attend_folded", "sfv_stale_topk_workspace_bytes", "sfv_stale_topk", "sfv_draft_tree",
     "sfv_attend_trays", "sfv_reject_workspace_bytes", "sfv_reject_verify", "sfv_match_trays",
+    "sfv_lm_head_greedy_bytes", "sfv_lm_head_greedy", "sfv_commit_greedy_workspace_bytes",
+    "sfv_commit_greedy",
 ]
 
 _lib = None
@@ -68,6 +70,10 @@ def load(path: str = LIB_PATH):
     lib.sfv_commit_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_commit.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P, SZ, P]
     lib.sfv_match_tree.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
+    lib.sfv_lm_head_greedy_bytes.argtypes = [I, I, I, ctypes.POINTER(SZ)]
+    lib.sfv_lm_head_greedy.argtypes = [P, P, I, I, P, I, I, P, P, SZ, P]
+    lib.sfv_commit_greedy_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
+    lib.sfv_commit_greedy.argtypes = [P, SZ, I, P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, SZ, P]
     lib.sfv_selfcheck_bounds.argtypes = [P, P]
     lib.sfv_stale_topk_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_stale_topk.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, SZ, P]
@@ -160,6 +166,37 @@ def sfv_commit(logits, rows, M, state, parent_host, B1, N, V, temperature, seed,
         float(temperature), int(seed) & (2**64 - 1), int(step0) & (2**64 - 1), int(pos0), k_max,
         float(tau), _ptr(next_state), _ptr(commit_pos), _ptr(token), _ptr(conf), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
+
+
+def sfv_lm_head_greedy_bytes(M, V, D) -> int:
+    """Bytes of the strip partials, or 0 where the shape is not served."""
+    lib = load()
+    out = ctypes.c_size_t(0)
+    rc = lib.sfv_lm_head_greedy_bytes(M, V, D, ctypes.byref(out))
+    if rc == SFV_E_UNSUPPORTED:
+        return 0
+    _check(rc)
+    return out.value
+
+
+def sfv_lm_head_greedy(hidden, rows, M, R, w, D, V, logits, partials, partials_bytes, stream=None):
+    return _check(load().sfv_lm_head_greedy(_ptr(hidden), _ptr(rows), M, R, _ptr(w), D, V, _ptr(logits),
+                                            _ptr(partials), int(partials_bytes), _stream(stream)))
+
+
+def sfv_commit_greedy_workspace_bytes(B1, N, M, V) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().sfv_commit_greedy_workspace_bytes(B1, N, M, V, ctypes.byref(out)))
+    return out.value
+
+
+def sfv_commit_greedy(partials, partials_bytes, D, logits, rows, M, state, parent_host, B1, N, V, k_max, tau,
+                      next_state, commit_pos, token, conf, workspace, workspace_bytes, stream=None):
+    par = _host_i32(parent_host)
+    return _check(load().sfv_commit_greedy(
+        _ptr(partials), int(partials_bytes), D, _ptr(logits), _ptr(rows), M, _ptr(state),
+        ctypes.cast(par, ctypes.c_void_p), B1, N, V, k_max, float(tau), _ptr(next_state), _ptr(commit_pos),
+        _ptr(token), _ptr(conf), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def sfv_match_tree(state, next_state, commit_pos, parent_host, B1, N, k_max, S_max, chain,

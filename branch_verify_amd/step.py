@@ -32,7 +32,7 @@ class VerifyStep:
     """Buffers and calls of one multi-branch verification step of fixed shape."""
 
     def __init__(self, B1, N, L, Hq, Hkv, d, D, V, M, parent, temperature, seed, step0, pos0,
-                 S_max=-1, k_max=1, tau=0.0, device="cuda"):
+                 S_max=-1, k_max=1, tau=0.0, fuse=True, device="cuda"):
         sfv.load()
         self.B1, self.N, self.L, self.Hq, self.Hkv, self.d = B1, N, L, Hq, Hkv, d
         self.D, self.V, self.M = D, V, M
@@ -51,6 +51,14 @@ class VerifyStep:
         self.logits = torch.empty((max(1, M), V), dtype=torch.float32, device=dev)
         self.commit_ws_bytes = sfv.sfv_commit_workspace_bytes(B1, N, M, V)
         self.commit_ws = torch.empty(max(1, self.commit_ws_bytes), dtype=torch.uint8, device=dev)
+        # greedy steps in the weight-streaming regime: the LM head writes tile
+        # partials and the commit reads those instead of the logits
+        self.parts_bytes = sfv.sfv_lm_head_greedy_bytes(M, V, D) if (fuse and self.T == 0.0) else 0
+        self.fuse = self.parts_bytes > 0
+        if self.fuse:
+            self.parts = torch.empty(self.parts_bytes, dtype=torch.uint8, device=dev)
+            self.greedy_ws_bytes = sfv.sfv_commit_greedy_workspace_bytes(B1, N, M, V)
+            self.greedy_ws = torch.empty(max(1, self.greedy_ws_bytes), dtype=torch.uint8, device=dev)
         self.next_state = torch.empty((B1, N), dtype=torch.int32, device=dev)
         self.commit_pos = torch.empty((B1, self.k_max), dtype=torch.int32, device=dev)
         self.token = torch.empty(max(1, M), dtype=torch.int32, device=dev)
@@ -80,6 +88,27 @@ class VerifyStep:
                        self.pos0, self.k_max, self.tau, self.next_state, self.commit_pos, self.token, self.conf,
                        self.commit_ws, self.commit_ws_bytes, stream)
 
+    def lm_head_greedy(self, x, stream=None):
+        sfv.sfv_lm_head_greedy(x["hidden"], self.rows, self.M, self.B1 * self.N, x["w"], self.D, self.V,
+                               self.logits, self.parts, self.parts_bytes, stream)
+
+    def commit_greedy(self, x, stream=None):
+        sfv.sfv_commit_greedy(self.parts, self.parts_bytes, self.D, self.logits, self.rows, self.M, x["state"],
+                              self.parent, self.B1, self.N, self.V, self.k_max, self.tau, self.next_state,
+                              self.commit_pos, self.token, self.conf, self.greedy_ws, self.greedy_ws_bytes,
+                              stream)
+
+    def head(self, x, stream=None):
+        """The LM head of the step (with tile partials when fused)."""
+        (self.lm_head_greedy if self.fuse else self.lm_head)(x, stream)
+
+    def commit_step(self, x, stream=None):
+        """The commit of the step (from the tile partials when fused)."""
+        if self.fuse:
+            self.commit_greedy(x, stream)
+        else:
+            self.commit(x, stream=stream)
+
     def match(self, x, stream=None):
         sfv.sfv_match_tree(x["state"], self.next_state, self.commit_pos, self.parent, self.B1,
                            self.N, self.k_max, self.S_max, self.chain, self.n_accepted, self.status, stream)
@@ -92,12 +121,14 @@ class VerifyStep:
         in order on `stream`.  attn_with="commit" starts it when the LM head
         is done, beside the commit and the walk (the LM head keeps the whole
         GPU); attn_with="lm_head" (the default, measured faster: the commit's
-        sweep also fills the GPU) starts it with the LM head."""
+        sweep also fills the GPU) starts it with the LM head.  Greedy steps in
+        the weight-streaming regime (with fuse) commit from the LM head's tile
+        partials."""
         if not overlap:
             self.attend(x, stream)
             self.masked_rows(x, stream)
-            self.lm_head(x, stream)
-            self.commit(x, stream=stream)
+            self.head(x, stream)
+            self.commit_step(x, stream)
             self.match(x, stream)
             return
         main = torch.cuda.current_stream() if stream is None else stream
@@ -108,12 +139,12 @@ class VerifyStep:
         if attn_with == "lm_head":
             self._fork.record(main)
         self.masked_rows(x, main)
-        self.lm_head(x, main)
+        self.head(x, main)
         if attn_with != "lm_head":
             self._fork.record(main)
         self._side.wait_event(self._fork)
         self.attend(x, self._side)
-        self.commit(x, stream=main)
+        self.commit_step(x, main)
         self.match(x, main)
         self._join.record(self._side)
         main.wait_event(self._join)
@@ -149,12 +180,12 @@ class VerifyStep:
             h=int(self.n_accepted.item()), status=int(self.status.item()))
 
 
-def step_for(wl, inp: dict, device="cuda", S_max=None, k_max=1, tau=0.0) -> VerifyStep:
+def step_for(wl, inp: dict, device="cuda", S_max=None, k_max=1, tau=0.0, fuse=True) -> VerifyStep:
     from .synth import masked_count
     M = masked_count(inp["state"])
     return VerifyStep(wl.B1, wl.N, wl.L, wl.Hq, wl.Hkv, wl.d, wl.D, wl.V, M, inp["parent"], wl.T,
                       wl.seed, wl.step0, wl.pos0, S_max=wl.S_t if S_max is None else S_max,
-                      k_max=k_max, tau=tau, device=device)
+                      k_max=k_max, tau=tau, fuse=fuse, device=device)
 
 
 class FoldedAttention:

@@ -313,6 +313,40 @@ int sfv_commit(const float* logits, const int32_t* rows, int M,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Greedy (T = 0) LM head and commit over tile partials: sfv_lm_head_greedy
+ * then sfv_commit_greedy give the outputs of sfv_lm_head then sfv_commit at
+ * temperature 0 (the same logits, tokens, committed positions and next
+ * states; conf within the same fp32 fast-path bound), without a second pass
+ * over the logits.  SpecFold, Appendix B (the head is a dense product over the
+ * masked rows); SPOT, "Important context" (at T = 0 the commit is the greedy
+ * argmax).
+ *
+ * sfv_lm_head_greedy: as sfv_lm_head, and the weight-streaming kernel also
+ * reduces every 128-id vocabulary tile of every row to its max, the lowest id
+ * attaining it and a fast fp32 sum of exp(l - max) with a bound on its error.
+ *   partials: device buffer of sfv_lm_head_greedy_bytes(M, V, D) bytes,
+ *   16-byte aligned, written whole (contents are internal to the pair).
+ * sfv_commit_greedy: merges the partials of each row (fast factors within the
+ * same bound, then fp64) and ranks, selects and writes exactly as sfv_commit
+ * does at T = 0, recomputing S in fp64 from the logits wherever the bound
+ * leaves the ranking or a tau decision open.
+ *   partials, D: as written by sfv_lm_head_greedy for the same M, V, D;
+ *   logits, rows, state, parent_host, outputs: as for sfv_commit;
+ *   workspace: sfv_commit_greedy_workspace_bytes(B1, N, M, V) bytes.
+ * Supported: 129 <= M <= 256 (the weight-streaming regime), D % 64 == 0 and
+ * D >= 128 (other shapes return SFV_E_UNSUPPORTED), V % 8 == 0,
+ * V < 2^31 / 8, 1 <= k_max <= N, tau finite when k_max > 1.
+ */
+int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes);
+int sfv_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w, int D, int V,
+                       float* logits, void* partials, size_t partials_bytes, void* stream);
+int sfv_commit_greedy_workspace_bytes(int B1, int N, int M, int V, size_t* bytes);
+int sfv_commit_greedy(const void* partials, size_t partials_bytes, int D, const float* logits,
+                      const int32_t* rows, int M, const int32_t* state, const int32_t* parent_host, int B1,
+                      int N, int V, int k_max, float tau, int32_t* next_state, int32_t* commit_pos,
+                      int32_t* token, float* conf, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * State-equality walk over the draft tree.  SpecFold, introduction (a later
  * main-branch state equal to a cached draft reuses its logits); SPOT, "How
  * does SPOT draft and verify?" (accept the longest prefix consistent with the

@@ -115,6 +115,58 @@ def test_commit_validation(lib):
     assert _commit(lib, [-1] + [0] * 64, B1=65) == sfv.SFV_E_INVAL
 
 
+def test_greedy_partials_validation(lib):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 151936, 4096)
+    assert rc == sfv.SFV_OK and nb == (151936 + 127) // 128 * 148 * 16
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 256, 1000, 128)
+    assert rc == sfv.SFV_OK and nb == 8 * 256 * 16
+    for M, D in [(128, 128), (257, 128), (0, 128), (148, 100), (148, 64)]:
+        assert _ws(lib.sfv_lm_head_greedy_bytes, M, 512, D)[0] == sfv.SFV_E_UNSUPPORTED, (M, D)
+    assert _ws(lib.sfv_lm_head_greedy_bytes, -1, 512, 128)[0] == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head_greedy_bytes(148, 512, 128, None) == sfv.SFV_E_INVAL
+    nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 512, 128)[1]
+    g = lib.sfv_lm_head_greedy
+    assert g(f, f, 100, 200, f, 128, 512, f, f, nb, None) == sfv.SFV_E_UNSUPPORTED
+    assert g(None, f, 148, 200, f, 128, 512, f, f, nb, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 200, f, 128, 512, f, None, nb, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 0, f, 128, 512, f, f, nb, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 200, f, 128, 512, f, P(0x1008), nb, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 200, f, 128, 512, f, f, nb - 16, None) == sfv.SFV_E_WORKSPACE
+
+
+def _commit_greedy(lib, parent, B1=9, N=32, M=148, V=512, D=128, k_max=1, tau=0.0, ws_bytes=None,
+                   parts_bytes=None, logits=0x1000):
+    P = ctypes.c_void_p
+    f = P(0x1000)
+    par = (ctypes.c_int32 * len(parent))(*parent)
+    if parts_bytes is None:
+        parts_bytes = 1 << 30
+    if ws_bytes is None:
+        ws_bytes = 1 << 30
+    return lib.sfv_commit_greedy(f, parts_bytes, D, P(logits), f, M, f, ctypes.cast(par, P), B1, N, V, k_max,
+                                 ctypes.c_float(tau), f, f, f, f, f, ws_bytes, None)
+
+
+def test_commit_greedy_validation(lib):
+    par = [-1] + list(range(8))
+    assert _ws(lib.sfv_commit_greedy_workspace_bytes, 9, 32, 148, 512)[0] == sfv.SFV_OK
+    assert _ws(lib.sfv_commit_greedy_workspace_bytes, 9, 32, 300, 512)[0] == sfv.SFV_E_INVAL
+    need = _ws(lib.sfv_commit_greedy_workspace_bytes, 9, 32, 148, 512)[1]
+    assert _commit_greedy(lib, [0] * 9) == sfv.SFV_E_TREE
+    assert _commit_greedy(lib, par, M=100) == sfv.SFV_E_UNSUPPORTED   # not the weight-streaming regime
+    assert _commit_greedy(lib, par, V=500) == sfv.SFV_E_UNSUPPORTED
+    assert _commit_greedy(lib, par, D=100) == sfv.SFV_E_UNSUPPORTED
+    assert _commit_greedy(lib, par, D=64) == sfv.SFV_E_UNSUPPORTED
+    assert _commit_greedy(lib, par, k_max=0) == sfv.SFV_E_INVAL
+    assert _commit_greedy(lib, par, k_max=33) == sfv.SFV_E_INVAL
+    assert _commit_greedy(lib, par, k_max=2, tau=float("nan")) == sfv.SFV_E_INVAL
+    assert _commit_greedy(lib, par, ws_bytes=need - 1) == sfv.SFV_E_WORKSPACE
+    assert _commit_greedy(lib, par, parts_bytes=16) == sfv.SFV_E_WORKSPACE
+    assert _commit_greedy(lib, par, logits=0x1004) == sfv.SFV_E_INVAL
+
+
 def test_commit_workspace_covers_every_tree(lib):
     for (B1, N, M, V) in [(3, 8, 10, 512), (9, 32, 144, 151936), (33, 64, 1478, 151936), (64, 256, 16384, 8)]:
         rc, need = _ws(lib.sfv_commit_workspace_bytes, B1, N, M, V)
