@@ -223,7 +223,7 @@ __device__ __forceinline__ void tile_store(Smem<D>& sm, int buf, const TileRegs<
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(Params p) {
   __shared__ Smem<D> sm;
   constexpr int DS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DB = D / 32;  // 32-wide output blocks of the head dim
