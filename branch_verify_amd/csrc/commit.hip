@@ -89,21 +89,18 @@ size_t ws_bytes(int B1, int N, int M, int items_max, int splits) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// g = -ln(-ln u), u = (w + 1/2) 2^-32, in fp32 with hardware log2.
+// g = -ln(-ln u), u = (w + 1/2) 2^-32, in fp32 with hardware log2.  Branch
+// free (the lanes of a wave take different cases): -ln u is log2 of u, or of
+// 1 - e with e = 1 - u for the upper half, or for e < 1/128 the series of
+// -ln(1 - e) to e^4; the same values as evaluating only the case that holds.
 __device__ __forceinline__ float gumbel_fast(unsigned w) {
   const float ln2 = 0.693147180559945309f;
-  float L1;  // -ln u > 0
-  if (w < 0x80000000u) {
-    const float u = ((float)w + 0.5f) * 2.3283064365386963e-10f;
-    L1 = -fast_log2(u) * ln2;
-  } else {
-    const float e = ((float)(~w) + 0.5f) * 2.3283064365386963e-10f;  // 1 - u, in (0, 1/2]
-    if (e < 0.0078125f) {
-      L1 = e * (1.f + e * (0.5f + e * (0.33333333f + e * 0.25f)));
-    } else {
-      L1 = -fast_log2(1.f - e) * ln2;
-    }
-  }
+  const bool upper = w >= 0x80000000u;
+  const float u = ((float)w + 0.5f) * 2.3283064365386963e-10f;
+  const float e = ((float)(~w) + 0.5f) * 2.3283064365386963e-10f;  // 1 - u, in (0, 1/2] when upper
+  const float ser = e * (1.f + e * (0.5f + e * (0.33333333f + e * 0.25f)));
+  const float lg = -fast_log2(upper ? 1.f - e : u) * ln2;
+  const float L1 = (upper && e < 0.0078125f) ? ser : lg;  // -ln u > 0
   return -fast_log2(L1) * ln2;
 }
 
@@ -205,6 +202,39 @@ __global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* ro
 // ---------------------------------------------------------------------------
 // vocabulary sweep of one work item over one vocab range
 // ---------------------------------------------------------------------------
+// Adds 8 consecutive ids v .. v + 7 of one row to its running max, first
+// argmax and confidence sum: one max update per 8 ids, the 8 fast terms
+// summed in fp32 (at most 7 roundings of a sum of positive terms: below
+// 2^-21 of it) and the group sum added in fp64, with the bound E.
+__device__ __forceinline__ void group8(const float (&x)[8], int v, float& lmax, int& lidx, double& S, float& E) {
+  float m8 = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, x[e]);
+  if (m8 > lmax) {
+    int e8 = 7;
+#pragma unroll
+    for (int e = 6; e >= 0; --e) e8 = x[e] == m8 ? e : e8;
+    if (lmax != -INFINITY) {
+      const float af = m8 - lmax;
+      const float f = fast_exp2(-af * kLog2e);
+      S *= (double)f;
+      E = E * f + (float)S * (kC1 * af + kC2);
+    }
+    lmax = m8;
+    lidx = v + e8;
+  }
+  float gs = 0.f, ga = 0.f;  // sum of terms, sum of term * argument
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float am = lmax - x[e];
+    const float tt = fast_exp2(-am * kLog2e);
+    gs += tt;
+    ga += tt * am;
+  }
+  S += (double)gs;
+  E += kC1 * ga + (kC2 + 4.76837158e-7f) * gs;
+}
+
 struct RowsArgs {
   const float* logits;
   const int32_t* rows;
@@ -261,17 +291,19 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
   // Logit loads are unconditional: a lane past the range end reads the last
   // 8 ids of the range and then drops them, so the compiler never has to
   // drain outstanding loads at a branch.
-  const float* rbase[R];
+  const float* rbase[R];  // rows past the item's last read that one again (an L1 hit, never used)
+  int last_row = row[0];
 #pragma unroll
-  for (int k = 0; k < R; ++k) rbase[k] = a.logits + (size_t)(k < nrows ? row[k] : row[0]) * a.V;
+  for (int k = 0; k < R; ++k) {
+    last_row = k < nrows ? row[k] : last_row;
+    rbase[k] = a.logits + (size_t)last_row * a.V;
+  }
   const int vlast = ve - 8;  // ve - vb >= 8: both are multiples of 8
 
   if constexpr (!NOISY) {
     // Greedy sweep.  Two iterations' logits are in flight in two register
     // sets used in turn (no register copies, which would make the compiler
-    // wait for the newest loads).  One max update per 8 ids; the 8 terms are
-    // summed in fp32 (at most 7 roundings of a sum of positive terms: below
-    // 2^-21 of it) and the group sum is added in fp64.
+    // wait for the newest loads).
     auto load8 = [&](float4& x0, float4& x1, int v) {
       const int vc = min(v, vlast);
       x0 = *(const float4*)(rbase[0] + vc);
@@ -280,32 +312,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
     auto take8 = [&](const float4& x0, const float4& x1, int v) {
       if (v >= ve) return;  // ve and v are multiples of 8
       const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      float m8 = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, x[e]);
-      if (m8 > lmax[0]) {
-        int e8 = 7;
-#pragma unroll
-        for (int e = 6; e >= 0; --e) e8 = x[e] == m8 ? e : e8;
-        if (lmax[0] != -INFINITY) {
-          const float af = m8 - lmax[0];
-          const float f = fast_exp2(-af * kLog2e);
-          S[0] *= (double)f;
-          E[0] = E[0] * f + (float)S[0] * (kC1 * af + kC2);
-        }
-        lmax[0] = m8;
-        lidx[0] = v + e8;
-      }
-      float gs = 0.f, ga = 0.f;  // sum of terms, sum of term * argument
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float am = lmax[0] - x[e];
-        const float tt = fast_exp2(-am * kLog2e);
-        gs += tt;
-        ga += tt * am;
-      }
-      S[0] += (double)gs;
-      E[0] += kC1 * ga + (kC2 + 4.76837158e-7f) * gs;
+      group8(x, v, lmax[0], lidx[0], S[0], E[0]);
     };
     float4 a0, a1, b0, b1;
     load8(a0, a1, vb + 8 * t);
@@ -321,10 +328,20 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
     // The trip count is uniform across the workgroup (cross-lane reductions
     // run inside the loop); a lane past the range end keeps every value at
     // -inf.
+    // Each row's logits are loaded two rows ahead of their use (the first two
+    // before the noise, whose arithmetic covers their latency); all loads are
+    // unconditional.
+    constexpr int kRowsAhead = 2;
     for (int v0 = vb; v0 < ve; v0 += kPerIter) {
       const int v = v0 + 8 * t;
       const bool active = v < ve;  // ve and v are multiples of 8
       const int vc = min(v, vlast);
+      float4 xa[R][2];
+#pragma unroll
+      for (int k = 0; k < kRowsAhead && k < R; ++k) {
+        xa[k][0] = *(const float4*)(rbase[k] + vc);
+        xa[k][1] = *(const float4*)(rbase[k] + vc + 4);
+      }
       unsigned wd[8];
       float gf[8];
       noise_block(a.seed, step, pos, (uint64_t)(v >> 3), wd);
@@ -334,33 +351,19 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
       // small arrays stay in registers)
 #pragma unroll
       for (int k = 0; k < R; ++k) {
+        if (k + kRowsAhead < R) {
+          xa[k + kRowsAhead][0] = *(const float4*)(rbase[k + kRowsAhead] + vc);
+          xa[k + kRowsAhead][1] = *(const float4*)(rbase[k + kRowsAhead] + vc + 4);
+        }
         if (k < nrows) {
-          const float4 x0 = *(const float4*)(rbase[k] + vc);
-          const float4 x1 = *(const float4*)(rbase[k] + vc + 4);
+          const float4 x0 = xa[k][0];
+          const float4 x1 = xa[k][1];
           // (an inactive lane's values are never used: the sums below are
           // guarded and its Gumbel keys are -inf)
           const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          // running max / first argmax and the confidence sum (this lane's ids)
-          if (active) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float xe = x[e];
-              if (xe > lmax[k]) {
-                if (lmax[k] != -INFINITY) {
-                  const float af = xe - lmax[k];
-                  const float f = fast_exp2(-af * kLog2e);
-                  S[k] *= (double)f;
-                  E[k] = E[k] * f + (float)S[k] * (kC1 * af + kC2);
-                }
-                lmax[k] = xe;
-                lidx[k] = v + e;
-              }
-              const float am = lmax[k] - xe;
-              const float tt = fast_exp2(-am * kLog2e);
-              S[k] += (double)tt;
-              E[k] += tt * (kC1 * am + kC2);
-            }
-          }
+          // running max / first argmax and the confidence sum (this lane's
+          // ids), one max update per 8 ids as in the greedy sweep
+          if (active) group8(x, v, lmax[k], lidx[k], S[k], E[k]);
           float ka[8], lm = -INFINITY;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
