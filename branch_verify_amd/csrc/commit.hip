@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
             ka[e] = active ? (x[e] * a.inv_t) + gf[e] : -INFINITY;
             lm = fmaxf(lm, ka[e]);
           }
-          wbest[k] = fmaxf(wbest[k], wave_max(lm));
+          wbest[k] = fmaxf(wbest[k], wave_max_dpp(lm));
           const float thr = wbest[k] - (2.f * kGumbelEps + 4.f * 1.1920929e-7f * fabsf(wbest[k]) + 1e-30f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {

@@ -60,6 +60,28 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Maximum over the 64 lanes of a wave, returned as a wave-uniform value:
+// rotations by 1, 2, 4 and 8 within each 16-lane row give every lane its
+// row's maximum, two row broadcasts carry rows 0-2 into row 3, and lane 63 is
+// read out.  All VALU (DPP) and one readlane, no LDS round trip; every lane
+// must be active.  The maximum does not depend on the order of combination, so
+// the result equals any other reduction's.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_keep(float x) {
+  // lanes outside the row mask (and lanes whose source is out of range) keep x
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), kCtrl, kRowMask, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_keep<0x121, 0xF>(v));  // row_ror:1
+  v = fmaxf(v, dpp_keep<0x122, 0xF>(v));  // row_ror:2
+  v = fmaxf(v, dpp_keep<0x124, 0xF>(v));  // row_ror:4
+  v = fmaxf(v, dpp_keep<0x128, 0xF>(v));  // row_ror:8
+  v = fmaxf(v, dpp_keep<0x142, 0xA>(v));  // row_bcast:15 into rows 1 and 3
+  v = fmaxf(v, dpp_keep<0x143, 0xC>(v));  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
