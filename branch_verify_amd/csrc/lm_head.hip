@@ -478,9 +478,9 @@ hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
 // Tile 256 vocab x 256 rows x 64 k, eight waves as 2 (vocab) x 4 (rows) of
 // 128 x 64, two waves per SIMD so that one wave's LDS traffic and barrier
 // waits overlap the other's MFMAs; double-buffered LDS (one workgroup per CU)
-// with the next k-tile prefetched into registers, and the fragments of the
-// next k-step read while the current one's MFMAs run.  A wave reads 3/4 KB of
-// LDS per MFMA (1 KB for the 64 x 64 wave tiles of lm_head_tiled).
+// with the next two k-tiles in flight in two register sets (with one, the
+// loads' latency under load outlasts a k-tile's MFMAs).  A wave reads 3/4 KB
+// of LDS per MFMA (1 KB for the 64 x 64 wave tiles of lm_head_tiled).
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_big8(Params p) {
   constexpr int NT = 512;
   constexpr int TVB = 256, BR = 256;
@@ -519,23 +519,25 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int hr = min(max(p.rows[m], 0), p.R - 1);  // never leave hidden
     hsrc[i] = p.hidden + (size_t)hr * p.D + (c % 8) * 8;
   }
-  u32x4 wreg[CA], hreg[CB];
-  auto fetch = [&](int k0) {
+  // two register sets: k-tile ks + 2 is loaded while ks + 1 waits in the
+  // other set for its turn in LDS
+  u32x4 wreg[2][CA], hreg[2][CB];
+  auto fetch = [&](int k0, int set) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) wreg[i] = ld16(wsrc[i] + k0);
+    for (int i = 0; i < CA; ++i) wreg[set][i] = ld16(wsrc[i] + k0);
 #pragma unroll
-    for (int i = 0; i < CB; ++i) hreg[i] = ld16(hsrc[i] + k0);
+    for (int i = 0; i < CB; ++i) hreg[set][i] = ld16(hsrc[i] + k0);
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, int set) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int c = t + NT * i;
-      st16(&ws[buf][c / 8][(c % 8) * 8], wreg[i]);
+      st16(&ws[buf][c / 8][(c % 8) * 8], wreg[set][i]);
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int c = t + NT * i;
-      st16(&hs[buf][c / 8][(c % 8) * 8], hreg[i]);
+      st16(&hs[buf][c / 8][(c % 8) * 8], hreg[set][i]);
     }
   };
   floatx16 acc[NA][NB];
@@ -546,37 +548,37 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
   const int ksteps = p.D / BK;
   const int klast = (ksteps - 1) * BK;
-  fetch(0);
-  stash(0);
+  fetch(0, 0);
+  fetch(min(BK, klast), 1);
+  stash(0, 0);
   __syncthreads();
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int buf = ks & 1;
-    fetch(min((ks + 1) * BK, klast));  // past the end: re-reads the last tile (L2 hit)
-    u32x4 fa[2][NA], fb[2][NB];
+  // k-tile ks is in LDS buffer ks & 1; its successor in register set
+  // (ks + 1) & 1; ks + 2 is loaded into set ks & 1 (past the end: re-reads of
+  // the last tile, L2 hits).  The loop is unrolled by four so that buffer and
+  // set indices are compile-time constants.
+  for (int ks0 = 0; ks0 < ksteps; ks0 += 4) {
 #pragma unroll
-    for (int a = 0; a < NA; ++a) fa[0][a] = ld16(&ws[buf][wv * 128 + a * 32 + col][half * 8]);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int ks = ks0 + jj;
+      if (ks >= ksteps) break;
+      const int buf = jj & 1;
+      fetch(min((ks + 2) * BK, klast), buf);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) fb[0][b] = ld16(&hs[buf][wm * 64 + b * 32 + col][half * 8]);
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        u32x4 fa[NA], fb[NB];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) {
+        for (int a = 0; a < NA; ++a) fa[a] = ld16(&ws[buf][wv * 128 + a * 32 + col][kk * 16 + half * 8]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) fb[b] = ld16(&hs[buf][wm * 64 + b * 32 + col][kk * 16 + half * 8]);
 #pragma unroll
         for (int a = 0; a < NA; ++a)
-          fa[cur ^ 1][a] = ld16(&ws[buf][wv * 128 + a * 32 + col][(kk + 1) * 16 + half * 8]);
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          fb[cur ^ 1][b] = ld16(&hs[buf][wm * 64 + b * 32 + col][(kk + 1) * 16 + half * 8]);
+          for (int b = 0; b < NB; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[a]), as_bf16x8(fb[b]), acc[a][b], 0, 0, 0);
       }
-#pragma unroll
-      for (int a = 0; a < NA; ++a)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[cur][a]), as_bf16x8(fb[cur][b]),
-                                                               acc[a][b], 0, 0, 0);
+      stash(buf ^ 1, buf ^ 1);
+      __syncthreads();
     }
-    stash(buf ^ 1);
-    __syncthreads();
   }
 
   // lane holds vocab v0 + wv*128 + a*32 + 8*(r/4) + 4*half + r%4 of row m0 + wm*64 + b*32 + col
