@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerIter = 8 * kThreads;  // vocab ids per workgroup iteration
-constexpr int kItemRows = 8;            // rows sharing one noise sweep
+constexpr int kItemRows = kItemRowsHost;  // rows sharing one noise sweep
 constexpr float kLog2e = kLog2eF;
 // error model of one fast term (internal.h): |t / exp(x - m) - 1| <= kC1 * a + kC2
 constexpr float kC1 = kExpC1;

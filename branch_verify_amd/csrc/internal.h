@@ -83,8 +83,10 @@ struct TreeArgs {
   unsigned char level_start[kMaxBranches + 1];
 };
 
-// Rows of equal (depth, position) share one noise sweep at T > 0, up to 8 per item.
-constexpr int kItemRowsHost = 8;
+// Rows of equal (depth, position) share one noise sweep at T > 0, up to 4 per
+// item (with 8, the per-row sweep state leaves room for only three waves per
+// SIMD, and the sweep runs slower despite fewer noise evaluations).
+constexpr int kItemRowsHost = 4;
 CommitPlan commit_plan(int B1, int N, int M, int V, int items_max, bool noisy);
 
 hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
