@@ -23,6 +23,9 @@
 //    the W path.  The reduction index k is permuted identically on both
 //    operands (slot (half, j) of step s holds k = 32*half + 8*s + j), which
 //    leaves the sum unchanged and makes a lane's 64 bytes per stage contiguous.
+//    Each quad of lanes loads whole 64-byte segments and a DPP quad transpose
+//    gives each lane its own (16-byte loads of one lane's segment, four rows
+//    per quad, reach the memory system as partial-line requests).
 //  * The gathered hidden rows (the operand the four waves share) are staged
 //    per 64-wide k-stage in double-buffered LDS.
 //  * Persistent workgroups (one or two per CU) walk their tiles over a
@@ -272,7 +275,35 @@ __device__ __forceinline__ void part_add(GreedyPart& r, const GreedyPart& e) {
   r.idx = idx;
 }
 
-template <int MB, int VW, int P, int OCC>
+// Quad transpose of 16-byte elements: element i of quad lane p becomes element
+// p of quad lane i (two butterfly stages of DPP quad permutations).  The
+// weight is loaded with each group of four lanes reading 64 contiguous bytes
+// of one row; the transpose then hands every lane the MFMA operand it needs.
+template <int kCtrl>
+__device__ __forceinline__ unsigned dpp_quad(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ void quad_transpose4(u32x4 (&a)[4]) {
+  const int p = threadIdx.x & 3;
+  u32x4 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = dpp_quad<0xB1>(a[i ^ 1][d]);  // quad_perm [1,0,3,2]
+    c[i] = (((i ^ p) & 1) == 0) ? a[i] : o;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = dpp_quad<0x4E>(c[i ^ 2][d]);  // quad_perm [2,3,0,1]
+    a[i] = (((i ^ p) & 2) == 0) ? c[i] : o;
+  }
+}
+
+template <int MB, int VW, int P, int OCC, bool QUAD = (OCC == 2)>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void lm_head_stream(Params p) {
   constexpr int MP = MB * 32;
   // LDS rows allocated: with OCC = 1, at least 81 KB, so that one workgroup fills a CU
@@ -302,11 +333,18 @@ __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(O
     const int hr = min(max(p.rows[m], 0), p.R - 1);  // never leave hidden
     hsrc[i] = p.hidden + (size_t)hr * p.D + (c % (SK / 8)) * 8;
   }
-  const unsigned short* wlane = p.w + 32 * half;
+  // Lane (r, half) multiplies W row tile*TV + wave*32*VW + 32*b + r, k range
+  // [k0 + 32 half, +32) of each stage.  With QUAD, load s of quad q fetches
+  // that segment of quad lane s's (row, half), 16 bytes per lane of the quad,
+  // so each load instruction asks for 16 whole 64-byte segments instead of 64
+  // partial ones, and quad_transpose4 then puts every segment in its own lane
+  // (the one-workgroup-per-CU variants, with more rows, lack the registers
+  // for the transpose and load their own segments).
+  const int qsel = QUAD ? 4 * (lane / 4) : lane;
+  const int qpart = QUAD ? 8 * (lane % 4) : 0;
 
-  // this lane's W rows of a tile: tile*TV + wave*32*VW + 32*b + r.  W comes
-  // from HBM and is prefetched P stages ahead; hidden comes from L2 and is
-  // loaded one stage ahead (registers are the limit on prefetch depth).
+  // W comes from HBM and is prefetched P stages ahead; hidden comes from L2
+  // and is loaded one stage ahead (registers are the limit on prefetch depth).
   u32x4 wreg[P][VW][4];
   u32x4 hreg[MB];
   // Flattened stage g (clamped to the last one: a re-read, an L2 hit).
@@ -317,10 +355,12 @@ __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(O
     const int k0 = stage_k(g);
 #pragma unroll
     for (int b = 0; b < VW; ++b) {
-      const int v = min(tile * TV + wave * 32 * VW + 32 * b + r, p.V - 1);
-      const unsigned short* src = wlane + (size_t)v * p.D + k0;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wd[b][s] = ld16(src + 8 * s);
+      for (int s = 0; s < 4; ++s) {
+        const int pl = QUAD ? qsel + s : qsel;  // the lane whose segment this load fetches
+        const int v = min(tile * TV + wave * 32 * VW + 32 * b + pl % 32, p.V - 1);
+        wd[b][s] = ld16(p.w + (size_t)v * p.D + k0 + 32 * (pl / 32) + (QUAD ? qpart : 8 * s));
+      }
     }
   };
   auto load_h = [&](int g) {
@@ -355,6 +395,10 @@ __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(O
       const int g = g0 + j;
       const int buf = g & 1;
       load_h(g + 1);
+      if (QUAD) {
+#pragma unroll
+        for (int b = 0; b < VW; ++b) quad_transpose4(wreg[j][b]);
+      }
       // Every hidden fragment of the stage is read before the first MFMA (the
       // scheduling barrier keeps them together), so the stage pays one LDS
       // latency instead of one per fragment.
