@@ -525,12 +525,18 @@ hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
 // with the next two k-tiles in flight in two register sets (with one, the
 // loads' latency under load outlasts a k-tile's MFMAs).  A wave reads 3/4 KB
 // of LDS per MFMA (1 KB for the 64 x 64 wave tiles of lm_head_tiled).
+// The waves form WV (vocab) x 8/WV (rows) groups of NA x NB 32-blocks each:
+// <2, 4, 2> is 256 vocab x 256 rows (128 x 64 per wave); <4, 2, 3> is 256 x 192
+// (64 x 96 per wave), chosen when it pads the rows less (M = 384: two tiles
+// exactly, where 256-row tiles compute 512).
+template <int WV, int NA, int NB>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_big8(Params p) {
   constexpr int NT = 512;
-  constexpr int TVB = 256, BR = 256;
-  constexpr int NA = 4, NB = 2;           // 32-blocks per wave: 128 vocab x 64 rows
-  constexpr int CA = TVB * 8 / NT;        // 4 chunks of W per thread per k-tile
-  constexpr int CB = BR * 8 / NT;         // 4 of hidden
+  constexpr int WM = 8 / WV;
+  constexpr int TVB = WV * NA * 32, BR = WM * NB * 32;
+  constexpr int CA = TVB * 8 / NT;        // chunks of W per thread per k-tile
+  constexpr int CB = BR * 8 / NT;         // of hidden
+  static_assert(TVB * 8 % NT == 0 && BR * 8 % NT == 0, "tile rows must spread evenly over the threads");
   __shared__ unsigned short ws[2][TVB][LDK];
   __shared__ unsigned short hs[2][BR][LDK];
 
@@ -545,8 +551,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int wave = t / kWave;
   const int half = lane / 32;
   const int col = lane % 32;
-  const int wv = wave / 4;  // vocab half
-  const int wm = wave % 4;  // row quarter
+  const int wv = wave / WM;  // vocab group
+  const int wm = wave % WM;  // row group
 
   const unsigned short* wsrc[CA];
   const unsigned short* hsrc[CB];
@@ -611,9 +617,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int kk = 0; kk < BK / 16; ++kk) {
         u32x4 fa[NA], fb[NB];
 #pragma unroll
-        for (int a = 0; a < NA; ++a) fa[a] = ld16(&ws[buf][wv * 128 + a * 32 + col][kk * 16 + half * 8]);
+        for (int a = 0; a < NA; ++a) fa[a] = ld16(&ws[buf][wv * NA * 32 + a * 32 + col][kk * 16 + half * 8]);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) fb[b] = ld16(&hs[buf][wm * 64 + b * 32 + col][kk * 16 + half * 8]);
+        for (int b = 0; b < NB; ++b) fb[b] = ld16(&hs[buf][wm * NB * 32 + b * 32 + col][kk * 16 + half * 8]);
 #pragma unroll
         for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -628,14 +634,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // lane holds vocab v0 + wv*128 + a*32 + 8*(r/4) + 4*half + r%4 of row m0 + wm*64 + b*32 + col
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int m = m0 + wm * 64 + b * 32 + col;
+    const int m = m0 + wm * NB * 32 + b * 32 + col;
     if (m >= p.M) continue;
     float* out = p.logits + (size_t)m * p.V;
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int v = v0 + wv * 128 + a * 32 + 8 * q4 + 4 * half;
+        const int v = v0 + wv * NA * 32 + a * 32 + 8 * q4 + 4 * half;
         const float4 val = make_float4(acc[a][b][4 * q4], acc[a][b][4 * q4 + 1], acc[a][b][4 * q4 + 2],
                                        acc[a][b][4 * q4 + 3]);
         if (v + 3 < p.V && (p.V % 4) == 0) {
@@ -653,8 +659,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 
 hipError_t launch_big8(const Params& p, hipStream_t stream) {
   const int vt = (p.V + 255) / 256;
-  const int mt = (p.M + 255) / 256;
-  hipLaunchKernelGGL(lm_head_big8, dim3(vt * mt), dim3(512), 0, stream, p);
+  const int pad256 = (p.M + 255) / 256 * 256, pad192 = (p.M + 191) / 192 * 192;
+  if (pad192 + 32 <= pad256) {
+    hipLaunchKernelGGL((lm_head_big8<4, 2, 3>), dim3(vt * ((p.M + 191) / 192)), dim3(512), 0, stream, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((lm_head_big8<2, 4, 2>), dim3(vt * ((p.M + 255) / 256)), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
