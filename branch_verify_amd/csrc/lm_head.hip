@@ -58,6 +58,7 @@ struct Params {
   int M, D, V, R;
   int vt, mt;          // tile counts
   GreedyPart* gpart;   // weight-streaming kernel only: tile partials [vocab tiles][M], or null
+  int big_a, big_b;    // large-tile kernel: row tiles of 256 rows, then of 192
 };
 
 __global__ __launch_bounds__(kThreads) void lm_head_tiled(Params p) {
@@ -527,25 +528,21 @@ hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
 // of LDS per MFMA (1 KB for the 64 x 64 wave tiles of lm_head_tiled).
 // The waves form WV (vocab) x 8/WV (rows) groups of NA x NB 32-blocks each:
 // <2, 4, 2> is 256 vocab x 256 rows (128 x 64 per wave); <4, 2, 3> is 256 x 192
-// (64 x 96 per wave), chosen when it pads the rows less (M = 384: two tiles
-// exactly, where 256-row tiles compute 512).
+// (64 x 96 per wave).  A launch mixes the two so that the rows are padded
+// least (M = 384: two 192-row tiles; M = 402: one of each, 448 rows, where
+// 256-row tiles alone compute 512).
+constexpr int kBigV = 256, kBigRows = 256;  // LDS rows of the large-tile kernel
+
 template <int WV, int NA, int NB>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_big8(Params p) {
+__device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsigned short (*ws)[kBigV][LDK],
+                                         unsigned short (*hs)[kBigRows][LDK]) {
   constexpr int NT = 512;
   constexpr int WM = 8 / WV;
   constexpr int TVB = WV * NA * 32, BR = WM * NB * 32;
   constexpr int CA = TVB * 8 / NT;        // chunks of W per thread per k-tile
   constexpr int CB = BR * 8 / NT;         // of hidden
   static_assert(TVB * 8 % NT == 0 && BR * 8 % NT == 0, "tile rows must spread evenly over the threads");
-  __shared__ unsigned short ws[2][TVB][LDK];
-  __shared__ unsigned short hs[2][BR][LDK];
-
-  const int mtiles = (p.M + BR - 1) / BR;
-  const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int mt = lid % mtiles;
-  const int vt = lid / mtiles;
-  const int v0 = vt * TVB;
-  const int m0 = mt * BR;
+  static_assert(TVB <= kBigV && BR <= kBigRows, "tile larger than its LDS");
   const int t = threadIdx.x;
   const int lane = t % kWave;
   const int wave = t / kWave;
@@ -657,14 +654,40 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 }
 
-hipError_t launch_big8(const Params& p, hipStream_t stream) {
-  const int vt = (p.V + 255) / 256;
-  const int pad256 = (p.M + 255) / 256 * 256, pad192 = (p.M + 191) / 192 * 192;
-  if (pad192 + 32 <= pad256) {
-    hipLaunchKernelGGL((lm_head_big8<4, 2, 3>), dim3(vt * ((p.M + 191) / 192)), dim3(512), 0, stream, p);
-    return hipGetLastError();
+// One launch covers the rows with big_a tiles of 256 rows and then big_b of
+// 192; the row tiles of one vocab tile get consecutive logical ids on one XCD.
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_big8(Params p) {
+  __shared__ unsigned short ws[2][kBigV][LDK];
+  __shared__ unsigned short hs[2][kBigRows][LDK];
+  const int mtiles = p.big_a + p.big_b;
+  const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int mt = lid % mtiles;
+  const int v0 = (lid / mtiles) * kBigV;
+  if (mt < p.big_a) {
+    big_tile<2, 4, 2>(p, v0, mt * 256, ws, hs);
+  } else {
+    big_tile<4, 2, 3>(p, v0, p.big_a * 256 + (mt - p.big_a) * 192, ws, hs);
   }
-  hipLaunchKernelGGL((lm_head_big8<2, 4, 2>), dim3(vt * ((p.M + 255) / 256)), dim3(512), 0, stream, p);
+}
+
+hipError_t launch_big8(const Params& p0, hipStream_t stream) {
+  // a tiles of 256 rows and b of 192 covering M with the fewest padded rows
+  // (ties: more 256-row tiles, whose waves read less LDS per MFMA)
+  Params p = p0;
+  int best_a = (p.M + 255) / 256, best_b = 0, best_pad = best_a * 256 - p.M;
+  for (int a = best_a - 1; a >= 0; --a) {
+    const int b = (p.M - 256 * a + 191) / 192;
+    const int pad = 256 * a + 192 * b - p.M;
+    if (pad < best_pad) {
+      best_a = a;
+      best_b = b;
+      best_pad = pad;
+    }
+  }
+  p.big_a = best_a;
+  p.big_b = best_b;
+  const int vt = (p.V + kBigV - 1) / kBigV;
+  hipLaunchKernelGGL(lm_head_big8, dim3(vt * (best_a + best_b)), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -690,6 +713,7 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   p.vt = (V + BV - 1) / BV;
   p.mt = (M + BM - 1) / BM;
   p.gpart = nullptr;
+  p.big_a = p.big_b = 0;
   // Up to 128 rows (one row tile): the tiled kernel.  129..256 rows: stream
   // the weight once past every row.  More rows: the large-tile kernel.
   if (M <= BM) return launch_tiled(p, stream);
@@ -721,6 +745,7 @@ hipError_t launch_lm_head_greedy(const void* hidden, const int32_t* rows, int M,
   p.vt = (V + BV - 1) / BV;
   p.mt = (M + BM - 1) / BM;
   p.gpart = gpart;
+  p.big_a = p.big_b = 0;
   return launch_stream_rows(p, stream);
 }
 
