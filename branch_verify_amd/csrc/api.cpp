@@ -376,8 +376,8 @@ int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes) {
   if (M < 0 || V < 1 || D < 1) return fail(SFV_E_INVAL, "M=%d, V=%d, D=%d out of range", M, V, D);
   const int ns = sfv::lm_head_greedy_parts(M, V, D);
   if (ns == 0) {
-    return fail(SFV_E_UNSUPPORTED, "greedy partials need 129 <= M <= 256, D %% 64 == 0 and D >= 128 (M=%d, D=%d)",
-                M, D);
+    return fail(SFV_E_UNSUPPORTED,
+                "greedy partials need M >= 129, D %% 64 == 0 and, for M <= 256, D >= 128 (M=%d, D=%d)", M, D);
   }
   *bytes = (size_t)ns * M * sizeof(sfv::GreedyPart);
   return ok();

@@ -628,6 +628,29 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
     }
   }
 
+  if (p.gpart) {
+    // Greedy partial of every row over this 256-id vocab tile: a wave merges
+    // its NA strips in id order, then the WV vocab groups are merged in id
+    // order through LDS (past the k-loop's last barrier nothing reads the
+    // weight tiles).
+    GreedyPart* gx = reinterpret_cast<GreedyPart*>(&ws[0][0][0]);  // [WV][BR]
+    static_assert(WV * BR * sizeof(GreedyPart) <= sizeof(unsigned short) * kBigV * LDK, "LDS for partials");
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int vw = v0 + wv * NA * 32 + 4 * half;
+      GreedyPart r = strip_partial(acc[0][b], vw, p.V);
+#pragma unroll
+      for (int a = 1; a < NA; ++a) part_add(r, strip_partial(acc[a][b], vw + a * 32, p.V));
+      if (half == 0) gx[wv * BR + wm * NB * 32 + b * 32 + col] = r;
+    }
+    __syncthreads();
+    if (t < BR && m0 + t < p.M) {
+      GreedyPart r = gx[t];
+      for (int w = 1; w < WV; ++w) part_add(r, gx[w * BR + t]);
+      p.gpart[(size_t)(v0 / kBigV) * p.M + m0 + t] = r;
+    }
+  }
+
   // lane holds vocab v0 + wv*128 + a*32 + 8*(r/4) + 4*half + r%4 of row m0 + wm*64 + b*32 + col
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -657,8 +680,8 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
 // One launch covers the rows with big_a tiles of 256 rows and then big_b of
 // 192; the row tiles of one vocab tile get consecutive logical ids on one XCD.
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void lm_head_big8(Params p) {
-  __shared__ unsigned short ws[2][kBigV][LDK];
-  __shared__ unsigned short hs[2][kBigRows][LDK];
+  __shared__ __attribute__((aligned(16))) unsigned short ws[2][kBigV][LDK];
+  __shared__ __attribute__((aligned(16))) unsigned short hs[2][kBigRows][LDK];
   const int mtiles = p.big_a + p.big_b;
   const int lid = xcd_logical_block(blockIdx.x, gridDim.x);
   const int mt = lid % mtiles;
@@ -721,13 +744,16 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   return launch_big8(p, stream);
 }
 
-// The weight-streaming kernel (129..256 rows, one-wide vocab tiles of 128
-// ids) writes one greedy partial per row and vocab tile beside the logits.
+// From 129 rows on, the LM head writes one greedy partial per row and vocab
+// tile beside the logits: 128-id tiles in the weight-streaming kernel (up to
+// 256 rows), 256-id tiles in the large-tile kernel.
 int lm_head_greedy_parts(int M, int V, int D) {
-  // (two or more k-stages per tile: a barrier separates the reads of a tile's
-  // strip partials from the next tile's writes)
-  if (M <= BM || M > kStreamRows || D % 64 != 0 || D < 128 || V < 1) return 0;
-  return (V + 127) / 128;
+  if (M <= BM || D % 64 != 0 || V < 1) return 0;
+  // weight-streaming kernel: 128-id tiles; two or more k-stages per tile (a
+  // barrier separates the reads of a tile's strip partials from the next
+  // tile's writes)
+  if (M <= kStreamRows) return D >= 128 ? (V + 127) / 128 : 0;
+  return (V + kBigV - 1) / kBigV;  // large-tile kernel: 256-id tiles
 }
 
 hipError_t launch_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w,
@@ -746,6 +772,7 @@ hipError_t launch_lm_head_greedy(const void* hidden, const int32_t* rows, int M,
   p.mt = (M + BM - 1) / BM;
   p.gpart = gpart;
   p.big_a = p.big_b = 0;
+  if (M > kStreamRows) return launch_big8(p, stream);
   return launch_stream_rows(p, stream);
 }
 

@@ -321,9 +321,10 @@ int sfv_commit(const float* logits, const int32_t* rows, int M,
  * masked rows); SPOT, "Important context" (at T = 0 the commit is the greedy
  * argmax).
  *
- * sfv_lm_head_greedy: as sfv_lm_head, and the weight-streaming kernel also
- * reduces every 128-id vocabulary tile of every row to its max, the lowest id
- * attaining it and a fast fp32 sum of exp(l - max) with a bound on its error.
+ * sfv_lm_head_greedy: as sfv_lm_head, and the kernel also reduces every
+ * vocabulary tile of every row (128 ids up to 256 rows, 256 ids above) to its
+ * max, the lowest id attaining it and a fast fp32 sum of exp(l - max) with a
+ * bound on its error.
  *   partials: device buffer of sfv_lm_head_greedy_bytes(M, V, D) bytes,
  *   16-byte aligned, written whole (contents are internal to the pair).
  * sfv_commit_greedy: merges the partials of each row (fast factors within the
@@ -333,9 +334,9 @@ int sfv_commit(const float* logits, const int32_t* rows, int M,
  *   partials, D: as written by sfv_lm_head_greedy for the same M, V, D;
  *   logits, rows, state, parent_host, outputs: as for sfv_commit;
  *   workspace: sfv_commit_greedy_workspace_bytes(B1, N, M, V) bytes.
- * Supported: 129 <= M <= 256 (the weight-streaming regime), D % 64 == 0 and
- * D >= 128 (other shapes return SFV_E_UNSUPPORTED), V % 8 == 0,
- * V < 2^31 / 8, 1 <= k_max <= N, tau finite when k_max > 1.
+ * Supported: M >= 129, D % 64 == 0, and D >= 128 when M <= 256 (other shapes
+ * return SFV_E_UNSUPPORTED), V % 8 == 0, V < 2^31 / 8, 1 <= k_max <= N, tau
+ * finite when k_max > 1.
  */
 int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes);
 int sfv_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w, int D, int V,

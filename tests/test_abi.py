@@ -122,8 +122,11 @@ def test_greedy_partials_validation(lib):
     assert rc == sfv.SFV_OK and nb == (151936 + 127) // 128 * 148 * 16
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 256, 1000, 128)
     assert rc == sfv.SFV_OK and nb == 8 * 256 * 16
-    for M, D in [(128, 128), (257, 128), (0, 128), (148, 100), (148, 64)]:
+    for M, D in [(128, 128), (0, 128), (148, 100), (148, 64), (257, 100)]:
         assert _ws(lib.sfv_lm_head_greedy_bytes, M, 512, D)[0] == sfv.SFV_E_UNSUPPORTED, (M, D)
+    # above 256 rows: one partial per 256-id tile, D = 64 allowed
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 257, 1000, 64)
+    assert rc == sfv.SFV_OK and nb == 4 * 257 * 16
     assert _ws(lib.sfv_lm_head_greedy_bytes, -1, 512, 128)[0] == sfv.SFV_E_INVAL
     assert lib.sfv_lm_head_greedy_bytes(148, 512, 128, None) == sfv.SFV_E_INVAL
     nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 512, 128)[1]

@@ -112,6 +112,10 @@ def _compare(sweep, parts, state, N, k_max):
     (8, 32, 256, 128, 1024, 1, 0.0),
     (9, 32, 160, 320, 6216, 2, 0.0),
     (3, 64, 190, 128, 136, 4, 0.9),
+    (9, 32, 257, 64, 1000, 1, 0.0),
+    (12, 32, 384, 4096, 4104, 1, 0.0),
+    (14, 32, 402, 192, 2056, 2, 0.5),
+    (24, 32, 700, 128, 520, 3, 0.9),
 ])
 def test_partials_match_sweep(gpu_lib, B1, N, M, D, V, k_max, tau):
     rng = np.random.default_rng(M * 7 + V)
