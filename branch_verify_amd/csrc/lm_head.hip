@@ -8,14 +8,14 @@
 // 4 consecutive vocab ids of one row and stores them as one 16-byte write of
 // the row-major logits, and both gather the masked rows through `rows`.
 //
-// lm_head_tiled (M <= 128): 128 vocab x 128 rows x 64 k tiles, four waves of
+// lm_head_tiled (M <= 32): 128 vocab x 128 rows x 64 k tiles, four waves of
 // 64 x 64, double-buffered LDS with the next k-tile prefetched into registers.
 //
 // lm_head_big8 (M > 256, MFMA-bound): 256 x 256 tiles, eight waves of 128 x 64;
 // the row tiles of one vocab tile get consecutive logical ids on one XCD, so
 // the weight tile they share is read from HBM once and then hit in L2.
 //
-// lm_head_stream (129..256 rows, the weight-streaming regime):
+// lm_head_stream (33..256 rows, the weight-streaming regime):
 //  * Every row of the padded row set is in one workgroup, so W is read from
 //    HBM exactly once and no MFMA work is spent on more than 31 pad rows.
 //  * Each wave owns 32 vocab rows and loads them from HBM straight into the
@@ -49,6 +49,7 @@ constexpr int BM = 128;  // rows per tile
 constexpr int BK = 64;   // k per stage
 constexpr int LDK = BK + 8;
 constexpr int kStreamRows = 256;  // largest row count served by lm_head_stream
+constexpr int kTiledRows = 32;    // largest row count served by lm_head_tiled
 
 struct Params {
   const unsigned short* hidden;
@@ -494,11 +495,23 @@ hipError_t launch_stream(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// 129..256 rows.  Up to 160 rows two workgroups share a CU (2-stage prefetch,
+// 33..256 rows.  Up to 160 rows two workgroups share a CU (2-stage prefetch,
 // registers for two waves per SIMD); above that one workgroup per CU.
+template <int MB>
+hipError_t launch_stream_two(const Params& p, hipStream_t stream) {
+  if ((p.D / 64) % 2 == 0) return launch_stream<MB, 1, 2, 2>(p, stream);
+  return launch_stream<MB, 1, 1, 2>(p, stream);
+}
+
 hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
   const int ks = p.D / 64;
   switch ((p.M + 31) / 32) {
+    case 2:
+      return launch_stream_two<2>(p, stream);
+    case 3:
+      return launch_stream_two<3>(p, stream);
+    case 4:
+      return launch_stream_two<4>(p, stream);
     case 5:
       if (ks % 2 == 0) return launch_stream<5, 1, 2, 2>(p, stream);
       return launch_stream<5, 1, 1, 2>(p, stream);
@@ -737,18 +750,20 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   p.mt = (M + BM - 1) / BM;
   p.gpart = nullptr;
   p.big_a = p.big_b = 0;
-  // Up to 128 rows (one row tile): the tiled kernel.  129..256 rows: stream
-  // the weight once past every row.  More rows: the large-tile kernel.
-  if (M <= BM) return launch_tiled(p, stream);
+  // Up to 32 rows: the tiled kernel.  33..256 rows: stream the weight once
+  // past every row (from 33 rows on it beats the tiled kernel, whose row
+  // tile re-reads the hidden rows with one k-tile in flight).  More rows: the
+  // large-tile kernel.
+  if (M <= kTiledRows) return launch_tiled(p, stream);
   if (M <= kStreamRows) return launch_stream_rows(p, stream);
   return launch_big8(p, stream);
 }
 
-// From 129 rows on, the LM head writes one greedy partial per row and vocab
+// From 33 rows on, the LM head writes one greedy partial per row and vocab
 // tile beside the logits: 128-id tiles in the weight-streaming kernel (up to
 // 256 rows), 256-id tiles in the large-tile kernel.
 int lm_head_greedy_parts(int M, int V, int D) {
-  if (M <= BM || D % 64 != 0 || V < 1) return 0;
+  if (M <= kTiledRows || D % 64 != 0 || V < 1) return 0;
   // weight-streaming kernel: 128-id tiles; two or more k-stages per tile (a
   // barrier separates the reads of a tile's strip partials from the next
   // tile's writes)

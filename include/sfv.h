@@ -334,7 +334,7 @@ int sfv_commit(const float* logits, const int32_t* rows, int M,
  *   partials, D: as written by sfv_lm_head_greedy for the same M, V, D;
  *   logits, rows, state, parent_host, outputs: as for sfv_commit;
  *   workspace: sfv_commit_greedy_workspace_bytes(B1, N, M, V) bytes.
- * Supported: M >= 129, D % 64 == 0, and D >= 128 when M <= 256 (other shapes
+ * Supported: M >= 33, D % 64 == 0, and D >= 128 when M <= 256 (other shapes
  * return SFV_E_UNSUPPORTED), V % 8 == 0, V < 2^31 / 8, 1 <= k_max <= N, tau
  * finite when k_max > 1.
  */

@@ -122,16 +122,18 @@ def test_greedy_partials_validation(lib):
     assert rc == sfv.SFV_OK and nb == (151936 + 127) // 128 * 148 * 16
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 256, 1000, 128)
     assert rc == sfv.SFV_OK and nb == 8 * 256 * 16
-    for M, D in [(128, 128), (0, 128), (148, 100), (148, 64), (257, 100)]:
+    for M, D in [(32, 128), (0, 128), (148, 100), (148, 64), (257, 100), (64, 64)]:
         assert _ws(lib.sfv_lm_head_greedy_bytes, M, 512, D)[0] == sfv.SFV_E_UNSUPPORTED, (M, D)
     # above 256 rows: one partial per 256-id tile, D = 64 allowed
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 257, 1000, 64)
     assert rc == sfv.SFV_OK and nb == 4 * 257 * 16
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 33, 1000, 128)  # 33..128 rows: the streaming kernel too
+    assert rc == sfv.SFV_OK and nb == 8 * 33 * 16
     assert _ws(lib.sfv_lm_head_greedy_bytes, -1, 512, 128)[0] == sfv.SFV_E_INVAL
     assert lib.sfv_lm_head_greedy_bytes(148, 512, 128, None) == sfv.SFV_E_INVAL
     nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 512, 128)[1]
     g = lib.sfv_lm_head_greedy
-    assert g(f, f, 100, 200, f, 128, 512, f, f, nb, None) == sfv.SFV_E_UNSUPPORTED
+    assert g(f, f, 32, 200, f, 128, 512, f, f, nb, None) == sfv.SFV_E_UNSUPPORTED
     assert g(None, f, 148, 200, f, 128, 512, f, f, nb, None) == sfv.SFV_E_INVAL
     assert g(f, f, 148, 200, f, 128, 512, f, None, nb, None) == sfv.SFV_E_INVAL
     assert g(f, f, 148, 0, f, 128, 512, f, f, nb, None) == sfv.SFV_E_INVAL
@@ -158,7 +160,7 @@ def test_commit_greedy_validation(lib):
     assert _ws(lib.sfv_commit_greedy_workspace_bytes, 9, 32, 300, 512)[0] == sfv.SFV_E_INVAL
     need = _ws(lib.sfv_commit_greedy_workspace_bytes, 9, 32, 148, 512)[1]
     assert _commit_greedy(lib, [0] * 9) == sfv.SFV_E_TREE
-    assert _commit_greedy(lib, par, M=100) == sfv.SFV_E_UNSUPPORTED   # not the weight-streaming regime
+    assert _commit_greedy(lib, par, M=32) == sfv.SFV_E_UNSUPPORTED    # the tiled kernel writes no partials
     assert _commit_greedy(lib, par, V=500) == sfv.SFV_E_UNSUPPORTED
     assert _commit_greedy(lib, par, D=100) == sfv.SFV_E_UNSUPPORTED
     assert _commit_greedy(lib, par, D=64) == sfv.SFV_E_UNSUPPORTED

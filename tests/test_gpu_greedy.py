@@ -112,6 +112,9 @@ def _compare(sweep, parts, state, N, k_max):
     (8, 32, 256, 128, 1024, 1, 0.0),
     (9, 32, 160, 320, 6216, 2, 0.0),
     (3, 64, 190, 128, 136, 4, 0.9),
+    (2, 32, 33, 128, 1000, 1, 0.0),
+    (4, 32, 64, 4096, 2056, 1, 0.0),
+    (5, 32, 100, 192, 777 // 8 * 8, 2, 0.5),
     (9, 32, 257, 64, 1000, 1, 0.0),
     (12, 32, 384, 4096, 4104, 1, 0.0),
     (14, 32, 402, 192, 2056, 2, 0.5),
