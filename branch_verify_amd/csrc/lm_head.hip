@@ -305,7 +305,7 @@ __device__ __forceinline__ void quad_transpose4(u32x4 (&a)[4]) {
   }
 }
 
-template <int MB, int VW, int P, int OCC, bool QUAD = (OCC == 2)>
+template <int MB, int VW, int P, int OCC, int HS = 1, bool QUAD = (OCC == 2)>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void lm_head_stream(Params p) {
   constexpr int MP = MB * 32;
   // LDS rows allocated: with OCC = 1, at least 81 KB, so that one workgroup fills a CU
@@ -401,23 +401,28 @@ __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(O
 #pragma unroll
         for (int b = 0; b < VW; ++b) quad_transpose4(wreg[j][b]);
       }
-      // Every hidden fragment of the stage is read before the first MFMA (the
-      // scheduling barrier keeps them together), so the stage pays one LDS
-      // latency instead of one per fragment.
-      u32x4 hf[4][MB];
+      // The hidden fragments of a group of 4 / HS k-steps are all read before
+      // its first MFMA (the scheduling barrier keeps them together), so the
+      // group pays one LDS latency instead of one per fragment; HS > 1 trades
+      // that for registers.
+      constexpr int SPG = 4 / HS;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int hg = 0; hg < HS; ++hg) {
+        u32x4 hf[SPG][MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) hf[s][mb] = ld16(&hs[buf][mb * 32 + r][32 * half + 8 * s]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int s2 = 0; s2 < SPG; ++s2)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+          for (int mb = 0; mb < MB; ++mb) hf[s2][mb] = ld16(&hs[buf][mb * 32 + r][32 * half + 8 * (hg * SPG + s2)]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int s2 = 0; s2 < SPG; ++s2) {
 #pragma unroll
-          for (int b = 0; b < VW; ++b)
-            acc[b][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wreg[j][b][s]), as_bf16x8(hf[s][mb]),
-                                                                 acc[b][mb], 0, 0, 0);
+          for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int b = 0; b < VW; ++b)
+              acc[b][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wreg[j][b][hg * SPG + s2]),
+                                                                   as_bf16x8(hf[s2][mb]), acc[b][mb], 0, 0, 0);
+          }
         }
       }
       load_w(wreg[j], g + P);
@@ -486,17 +491,20 @@ int cu_count() {
   return cus[dev];
 }
 
-template <int MB, int VW, int P, int OCC = 1>
+template <int MB, int VW, int P, int OCC = 1, int HS = 1>
 hipError_t launch_stream(const Params& p, hipStream_t stream) {
   if ((p.D / 64) % P != 0) return hipErrorInvalidValue;
   const int ntiles = (p.V + 128 * VW - 1) / (128 * VW);
   const int grid = min(ntiles, OCC * cu_count());
-  hipLaunchKernelGGL((lm_head_stream<MB, VW, P, OCC>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((lm_head_stream<MB, VW, P, OCC, HS>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-// 33..256 rows.  Up to 160 rows two workgroups share a CU (2-stage prefetch,
-// registers for two waves per SIMD); above that one workgroup per CU.
+// 33..256 rows.  Up to 224 rows two workgroups share a CU (2-stage prefetch,
+// registers for two waves per SIMD; from 161 rows the hidden fragments are
+// read in groups to fit); above that one workgroup per CU.  Measured on the
+// SDAR-8B head: 192 rows 447 -> 409 us, 224 rows 517 -> 462 us against one
+// workgroup per CU.
 template <int MB>
 hipError_t launch_stream_two(const Params& p, hipStream_t stream) {
   if ((p.D / 64) % 2 == 0) return launch_stream<MB, 1, 2, 2>(p, stream);
@@ -515,11 +523,11 @@ hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
     case 5:
       if (ks % 2 == 0) return launch_stream<5, 1, 2, 2>(p, stream);
       return launch_stream<5, 1, 1, 2>(p, stream);
-    case 6:
-      if (ks % 4 == 0) return launch_stream<6, 1, 4, 1>(p, stream);
-      if (ks % 2 == 0) return launch_stream<6, 1, 2, 1>(p, stream);
-      return launch_stream<6, 1, 1, 1>(p, stream);
-    case 7:
+    case 6:  // two workgroups per CU fit with the hidden fragments read in halves
+      if (ks % 2 == 0) return launch_stream<6, 1, 2, 2, 2>(p, stream);
+      return launch_stream<6, 1, 1, 2, 4>(p, stream);
+    case 7:  // ... and here in quarters (256 registers, no spills)
+      if (ks % 2 == 0) return launch_stream<7, 1, 2, 2, 4>(p, stream);
       if (ks % 2 == 0) return launch_stream<7, 1, 2, 1>(p, stream);
       return launch_stream<7, 1, 1, 1>(p, stream);
     case 8:

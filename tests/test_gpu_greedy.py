@@ -115,6 +115,8 @@ def _compare(sweep, parts, state, N, k_max):
     (2, 32, 33, 128, 1000, 1, 0.0),
     (4, 32, 64, 4096, 2056, 1, 0.0),
     (5, 32, 100, 192, 777 // 8 * 8, 2, 0.5),
+    (7, 32, 170, 192, 1000, 1, 0.0),
+    (7, 32, 224, 4096, 2056, 2, 0.5),
     (9, 32, 257, 64, 1000, 1, 0.0),
     (12, 32, 384, 4096, 4104, 1, 0.0),
     (14, 32, 402, 192, 2056, 2, 0.5),
