@@ -11,11 +11,12 @@
 // lm_head_tiled (M <= 32): 128 vocab x 128 rows x 64 k tiles, four waves of
 // 64 x 64, double-buffered LDS with the next k-tile prefetched into registers.
 //
-// lm_head_big8 (M > 256, MFMA-bound): 256 x 256 tiles, eight waves of 128 x 64;
+// lm_head_big8 (M > 160; MFMA-bound from a few hundred rows): 256-id vocab tiles
+// of 256 or 192 rows, eight waves;
 // the row tiles of one vocab tile get consecutive logical ids on one XCD, so
 // the weight tile they share is read from HBM once and then hit in L2.
 //
-// lm_head_stream (33..256 rows, the weight-streaming regime):
+// lm_head_stream (33..160 rows, the weight-streaming regime):
 //  * Every row of the padded row set is in one workgroup, so W is read from
 //    HBM exactly once and no MFMA work is spent on more than 31 pad rows.
 //  * Each wave owns 32 vocab rows and loads them from HBM straight into the
@@ -48,7 +49,7 @@ constexpr int BV = 128;  // vocab per tile
 constexpr int BM = 128;  // rows per tile
 constexpr int BK = 64;   // k per stage
 constexpr int LDK = BK + 8;
-constexpr int kStreamRows = 256;  // largest row count served by lm_head_stream
+constexpr int kStreamRows = 160;  // largest row count served by lm_head_stream
 constexpr int kTiledRows = 32;    // largest row count served by lm_head_tiled
 
 struct Params {
@@ -500,11 +501,11 @@ hipError_t launch_stream(const Params& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// 33..256 rows.  Up to 224 rows two workgroups share a CU (2-stage prefetch,
-// registers for two waves per SIMD; from 161 rows the hidden fragments are
-// read in groups to fit); above that one workgroup per CU.  Measured on the
-// SDAR-8B head: 192 rows 447 -> 409 us, 224 rows 517 -> 462 us against one
-// workgroup per CU.
+// 33..160 rows: two workgroups share a CU (2-stage prefetch, registers for
+// two waves per SIMD).  Above 160 rows the large-tile kernel is faster (on the
+// SDAR-8B head: 397-401 against 418-421 us at 176-192 rows, 471-475 against
+// 530-796 us at 240-256): its 256-id vocab tiles re-read the hidden rows half
+// as often, and it needs no register-starved one-workgroup-per-CU variant.
 template <int MB>
 hipError_t launch_stream_two(const Params& p, hipStream_t stream) {
   if ((p.D / 64) % 2 == 0) return launch_stream<MB, 1, 2, 2>(p, stream);
@@ -523,16 +524,6 @@ hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
     case 5:
       if (ks % 2 == 0) return launch_stream<5, 1, 2, 2>(p, stream);
       return launch_stream<5, 1, 1, 2>(p, stream);
-    case 6:  // two workgroups per CU fit with the hidden fragments read in halves
-      if (ks % 2 == 0) return launch_stream<6, 1, 2, 2, 2>(p, stream);
-      return launch_stream<6, 1, 1, 2, 4>(p, stream);
-    case 7:  // ... and here in quarters (256 registers, no spills)
-      if (ks % 2 == 0) return launch_stream<7, 1, 2, 2, 4>(p, stream);
-      if (ks % 2 == 0) return launch_stream<7, 1, 2, 1>(p, stream);
-      return launch_stream<7, 1, 1, 1>(p, stream);
-    case 8:
-      if (ks % 2 == 0) return launch_stream<8, 1, 2, 1>(p, stream);
-      return launch_stream<8, 1, 1, 1>(p, stream);
     default:
       return hipErrorInvalidValue;
   }
@@ -758,7 +749,7 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   p.mt = (M + BM - 1) / BM;
   p.gpart = nullptr;
   p.big_a = p.big_b = 0;
-  // Up to 32 rows: the tiled kernel.  33..256 rows: stream the weight once
+  // Up to 32 rows: the tiled kernel.  33..160 rows: stream the weight once
   // past every row (from 33 rows on it beats the tiled kernel, whose row
   // tile re-reads the hidden rows with one k-tile in flight).  More rows: the
   // large-tile kernel.
@@ -769,7 +760,7 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
 
 // From 33 rows on, the LM head writes one greedy partial per row and vocab
 // tile beside the logits: 128-id tiles in the weight-streaming kernel (up to
-// 256 rows), 256-id tiles in the large-tile kernel.
+// 160 rows), 256-id tiles in the large-tile kernel.
 int lm_head_greedy_parts(int M, int V, int D) {
   if (M <= kTiledRows || D % 64 != 0 || V < 1) return 0;
   // weight-streaming kernel: 128-id tiles; two or more k-stages per tile (a

@@ -322,7 +322,7 @@ int sfv_commit(const float* logits, const int32_t* rows, int M,
  * argmax).
  *
  * sfv_lm_head_greedy: as sfv_lm_head, and the kernel also reduces every
- * vocabulary tile of every row (128 ids up to 256 rows, 256 ids above) to its
+ * vocabulary tile of every row (128 ids up to 160 rows, 256 ids above) to its
  * max, the lowest id attaining it and a fast fp32 sum of exp(l - max) with a
  * bound on its error.
  *   partials: device buffer of sfv_lm_head_greedy_bytes(M, V, D) bytes,
@@ -334,7 +334,7 @@ int sfv_commit(const float* logits, const int32_t* rows, int M,
  *   partials, D: as written by sfv_lm_head_greedy for the same M, V, D;
  *   logits, rows, state, parent_host, outputs: as for sfv_commit;
  *   workspace: sfv_commit_greedy_workspace_bytes(B1, N, M, V) bytes.
- * Supported: M >= 33, D % 64 == 0, and D >= 128 when M <= 256 (other shapes
+ * Supported: M >= 33, D % 64 == 0, and D >= 128 when M <= 160 (other shapes
  * return SFV_E_UNSUPPORTED), V % 8 == 0, V < 2^31 / 8, 1 <= k_max <= N, tau
  * finite when k_max > 1.
  */

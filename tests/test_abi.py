@@ -120,8 +120,10 @@ def test_greedy_partials_validation(lib):
     f = P(0x1000)
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 151936, 4096)
     assert rc == sfv.SFV_OK and nb == (151936 + 127) // 128 * 148 * 16
-    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 256, 1000, 128)
-    assert rc == sfv.SFV_OK and nb == 8 * 256 * 16
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 160, 1000, 128)
+    assert rc == sfv.SFV_OK and nb == 8 * 160 * 16
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 161, 1000, 64)  # above 160 rows: 256-id tiles
+    assert rc == sfv.SFV_OK and nb == 4 * 161 * 16
     for M, D in [(32, 128), (0, 128), (148, 100), (148, 64), (257, 100), (64, 64)]:
         assert _ws(lib.sfv_lm_head_greedy_bytes, M, 512, D)[0] == sfv.SFV_E_UNSUPPORTED, (M, D)
     # above 256 rows: one partial per 256-id tile, D = 64 allowed
