@@ -57,7 +57,6 @@ struct Partial {
 };
 
 struct WsLayout {
-  int32_t* rowmap;  // [B1*N] flat position -> row, -1 if not masked
   int32_t* count;   // [1] work items
   Item* items;      // [items_max]
   Partial* part;    // [M][splits]
@@ -69,8 +68,6 @@ __host__ __device__ inline WsLayout ws_layout(void* base, int B1, int N, int M, 
   char* b = (char*)base;
   WsLayout w;
   size_t off = 0;
-  w.rowmap = (int32_t*)(b + off);
-  off = align256(off + sizeof(int32_t) * (size_t)B1 * N);
   w.count = (int32_t*)(b + off);
   off = align256(off + 16);
   w.items = (Item*)(b + off);
@@ -80,8 +77,7 @@ __host__ __device__ inline WsLayout ws_layout(void* base, int B1, int N, int M, 
 }
 
 size_t ws_bytes(int B1, int N, int M, int items_max, int splits) {
-  size_t off = align256(sizeof(int32_t) * (size_t)B1 * N);
-  off = align256(off + 16);
+  size_t off = align256(16);
   off = align256(off + sizeof(Item) * (size_t)items_max);
   return off + sizeof(Partial) * (size_t)M * splits;
 }
@@ -145,20 +141,21 @@ __global__ __launch_bounds__(1024) void masked_rows_kernel(const int32_t* state,
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* rows, int M, int N,
                                                                TreeArgs tree, bool noisy, WsLayout ws) {
-  __shared__ int tsum[kThreads];
-  const int t = threadIdx.x;
-  const int total = tree.B1 * N;
-  for (int f = t; f < total; f += kThreads) ws.rowmap[f] = -1;
-  __syncthreads();
-  for (int r = t; r < M; r += kThreads) {
-    const int f = rows[r];
-    if (f >= 0 && f < total) ws.rowmap[f] = r;  // ids outside the block are ignored
-  }
-  __syncthreads();
+  __shared__ int wsum[kThreads / kWave];
+  __shared__ int rowmap[kMaxBranches * kMaxBlock];  // flat position -> row, -1 if not masked
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   if (!noisy) {
     if (t == 0) *ws.count = M;
     return;
   }
+  const int total = tree.B1 * N;
+  for (int f = t; f < total; f += kThreads) rowmap[f] = -1;
+  __syncthreads();
+  for (int r = t; r < M; r += kThreads) {
+    const int f = rows[r];
+    if (f >= 0 && f < total) rowmap[f] = r;  // ids outside the block are ignored
+  }
+  __syncthreads();
   // pairs p = level * N + n, contiguous ranges per thread
   const int pairs = tree.levels * N;
   const int per = (pairs + kThreads - 1) / kThreads;
@@ -168,13 +165,20 @@ __global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* ro
     const int lv = p / N, n = p % N;
     int cnt = 0;
     for (int a = tree.level_start[lv]; a < tree.level_start[lv + 1]; ++a)
-      cnt += ws.rowmap[tree.by_level[a] * N + n] >= 0;
+      cnt += rowmap[tree.by_level[a] * N + n] >= 0;
     mine += (cnt + kItemRows - 1) / kItemRows;
   }
-  tsum[t] = mine;
+  // exclusive prefix sum of the item counts over the threads, in thread order
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int up = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += up;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  int off = 0;
-  for (int u = 0; u < t; ++u) off += tsum[u];
+  int off = incl - mine;
+  for (int w = 0; w < wave; ++w) off += wsum[w];
   for (int p = pb; p < pe; ++p) {
     const int lv = p / N, n = p % N;
     Item it;
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* ro
     it.level = lv;
     it.pad = 0;
     for (int a = tree.level_start[lv]; a < tree.level_start[lv + 1]; ++a) {
-      const int r = ws.rowmap[tree.by_level[a] * N + n];
+      const int r = rowmap[tree.by_level[a] * N + n];
       if (r < 0) continue;
       it.rows[it.nrows++] = r;
       if (it.nrows == kItemRows) {
