@@ -3,18 +3,18 @@
 //
 // SpecFold, Appendix B, keeps the LM head as a plain dense library product;
 // here it is the dominant step of a one-layer verify pass: the weight is
-// ~1.2 GB of bf16 and must be streamed from HBM once per pass.  Both kernels
-// compute the product transposed (vocab x rows), so that each lane ends with
-// 4 consecutive vocab ids of one row and stores them as one 16-byte write of
-// the row-major logits, and both gather the masked rows through `rows`.
+// ~1.2 GB of bf16 and must be streamed from HBM once per pass.  All three
+// kernels compute the product transposed (vocab x rows), so that each lane
+// ends with 4 consecutive vocab ids of one row and stores them as one 16-byte
+// write of the row-major logits, and all gather the masked rows through `rows`.
 //
 // lm_head_tiled (M <= 32): 128 vocab x 128 rows x 64 k tiles, four waves of
 // 64 x 64, double-buffered LDS with the next k-tile prefetched into registers.
 //
-// lm_head_big8 (M > 160; MFMA-bound from a few hundred rows): 256-id vocab tiles
-// of 256 or 192 rows, eight waves;
-// the row tiles of one vocab tile get consecutive logical ids on one XCD, so
-// the weight tile they share is read from HBM once and then hit in L2.
+// lm_head_big8 (M > 160; MFMA-bound from a few hundred rows): 256-id vocab
+// tiles of 256 or 192 rows, eight waves, the next two k-tiles in flight; the
+// row tiles of one vocab tile get consecutive logical ids on one XCD, so the
+// weight tile they share is read from HBM once and then hit in L2.
 //
 // lm_head_stream (33..160 rows, the weight-streaming regime):
 //  * Every row of the padded row set is in one workgroup, so W is read from
