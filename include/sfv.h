@@ -265,8 +265,12 @@ int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t*
  * head is a plain dense product): logits[r][v] = sum_k hidden[rows[r]][k] * w[v][k].
  *   hidden [R][D] bf16 (R = B1*N, rows index it); rows [M] int32, each in [0, R)
  *   w      [V][D] bf16;  logits [M][V] fp32 (fp32 accumulation)
- * Supported: D % 64 == 0, 1 <= V, 0 <= M.  Row ids are not range-checked on
- * the device: the caller guarantees 0 <= rows[r] < R.
+ * Supported: D % 64 == 0, 1 <= V, 0 <= M.  Row ids should lie in [0, R); the
+ * kernels clamp any outside it into that range (no error is reported), so a
+ * bad id yields that clamped row's logits but never an access outside hidden.
+ * Kernel by M: up to 32 rows a tiled kernel, 33..160 a weight-streaming kernel
+ * (the weight read from HBM once past every row), above that 256-id vocab
+ * tiles of 256 or 192 rows.
  */
 int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R,
                 const void* w, int D, int V, float* logits, void* stream);
