@@ -248,7 +248,8 @@ struct RowsArgs {
   uint64_t seed, step0, pos0;
 };
 
-template <bool NOISY, int R>
+// UNIT_T: T = 1, where l * (1/T) = l exactly and the multiply is left out.
+template <bool NOISY, int R, bool UNIT_T = false>
 __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLayout ws) {
   __shared__ float red_f[kThreads / kWave][R][2];
   __shared__ int red_i[kThreads / kWave][R][2];
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
           float ka[8], lm = -INFINITY;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            ka[e] = active ? (x[e] * a.inv_t) + gf[e] : -INFINITY;
+            ka[e] = active ? (UNIT_T ? x[e] : x[e] * a.inv_t) + gf[e] : -INFINITY;
             lm = fmaxf(lm, ka[e]);
           }
           wbest[k] = fmaxf(wbest[k], wave_max_dpp(lm));
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             if (active && ka[e] >= thr) {
-              const float key = (x[e] * a.inv_t) + gumbel_exact(wd[e]);
+              const float key = (UNIT_T ? x[e] : x[e] * a.inv_t) + gumbel_exact(wd[e]);
               if (key > kmax[k]) {
                 kmax[k] = key;
                 kidx[k] = v + e;
@@ -932,10 +933,13 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
     ra.step0 = step0;
     ra.pos0 = (uint64_t)pos0;
     const unsigned blocks = (unsigned)plan.items_max * plan.splits;
-    if (noisy)
+    if (noisy && ra.inv_t == 1.0f) {
+      hipLaunchKernelGGL((commit_rows_kernel<true, kItemRows, true>), dim3(blocks), dim3(kThreads), 0, stream, ra, ws);
+    } else if (noisy) {
       hipLaunchKernelGGL((commit_rows_kernel<true, kItemRows>), dim3(blocks), dim3(kThreads), 0, stream, ra, ws);
-    else
+    } else {
       hipLaunchKernelGGL((commit_rows_kernel<false, 1>), dim3(blocks), dim3(kThreads), 0, stream, ra, ws);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
