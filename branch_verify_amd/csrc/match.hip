@@ -6,10 +6,11 @@
 // the target accepts the longest prefix consistent with its own trajectory;
 // with shared noise that is state equality (Proposition 2).
 //
-// One workgroup of four waves.  Phase 1 spreads the 2*B1 rows (every drafted
-// state and every next state) over the waves: each wave checks a draft
-// against its parent and folds a row into a 64-bit hash, sum over positions
-// of mix(n, token) (order-free, so the lanes reduce it with shuffles).
+// One workgroup of four waves.  Phase 1 spreads the (row, position) elements
+// of the 2*B1 rows (every drafted state and every next state) over all
+// threads, so their loads are issued together: each row's 64-bit hash is the
+// sum over positions of mix(n, token), order-free, so LDS atomic adds build
+// it; every draft position is checked against its parent's.
 // Phase 2 is the walk, in wave 0: each hop ballots the drafts whose hash
 // equals the current next state and confirms the lowest candidate by a full,
 // coalesced comparison, so a hash collision can never produce a false match.
@@ -30,53 +31,46 @@ __device__ __forceinline__ uint64_t mix(uint64_t x) {
   return x ^ (x >> 31);
 }
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned lo = __shfl_xor((unsigned)v, o, kWave);
-    const unsigned hi = __shfl_xor((unsigned)(v >> 32), o, kWave);
-    v += ((uint64_t)hi << 32) | lo;
-  }
-  return v;
-}
-
 __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, const int32_t* next_state,
                                                          const int32_t* commit_pos, TreeArgs tree, int N,
                                                          int k_max, int S_max, int32_t* chain,
                                                          int32_t* n_accepted, int32_t* status) {
-  __shared__ uint64_t hs[kMaxBranches];  // hash of state[i]
-  __shared__ uint64_t hn[kMaxBranches];  // hash of next_state[i]
+  __shared__ unsigned long long hs[kMaxBranches];  // hash of state[i]
+  __shared__ unsigned long long hn[kMaxBranches];  // hash of next_state[i]
+  __shared__ int fresh[kMaxBranches];              // positions a draft unmasks over its parent
   __shared__ int bad_s;
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int B1 = tree.B1;
+  if (t < B1) {
+    hs[t] = 0ull;
+    hn[t] = 0ull;
+    fresh[t] = 0;
+  }
   if (t == 0) bad_s = 0;
   __syncthreads();
 
-  for (int row = wave; row < 2 * B1; row += kThreads / kWave) {
+  // Every (row, position) of the 2*B1 rows at once: the hashes are sums, so
+  // their order does not matter and LDS atomic adds build them; each draft
+  // position is also checked against its parent's.
+  const int elems = 2 * B1 * N;
+  for (int e = t; e < elems; e += kThreads) {
+    const int row = e / N, n = e % N;
     const bool is_next = row >= B1;
     const int i = is_next ? row - B1 : row;
-    const int32_t* src = (is_next ? next_state : state) + (size_t)i * N;
-    uint64_t h = 0;
-    for (int n = lane; n < N; n += kWave) h += mix(((uint64_t)(uint32_t)n << 32) | (uint32_t)src[n]);
-    h = wave_sum_u64(h);
-    if (lane == 0) (is_next ? hn : hs)[i] = h;
+    const int v = (is_next ? next_state : state)[(size_t)i * N + n];
+    atomicAdd(&(is_next ? hn : hs)[i], (unsigned long long)mix(((uint64_t)(uint32_t)n << 32) | (uint32_t)v));
     if (!is_next && S_max >= 0 && i >= 1) {
       // a draft keeps every unmasked token of its parent and unmasks at most S_max more
-      const int32_t* par = state + (size_t)tree.parent[i] * N;
-      bool bad = false;
-      int fresh = 0;
-      for (int n = lane; n < N; n += kWave) {
-        const int sp = par[n], sc = src[n];
-        if (sp != -1) bad = bad || (sc != sp);
-        else fresh += (sc != -1);
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) fresh += __shfl_xor(fresh, o, kWave);
-      if (__any(bad) || fresh > S_max) {
-        if (lane == 0) bad_s = 1;
+      const int sp = state[(size_t)tree.parent[i] * N + n];
+      if (sp != -1) {
+        if (v != sp) bad_s = 1;
+      } else if (v != -1) {
+        atomicAdd(&fresh[i], 1);
       }
     }
   }
+  __syncthreads();
+  if (S_max >= 0 && t >= 1 && t < B1 && fresh[t] > S_max) bad_s = 1;
   __syncthreads();
 
   if (wave != 0) return;
