@@ -121,6 +121,8 @@ def _compare(sweep, parts, state, N, k_max):
     (12, 32, 384, 4096, 4104, 1, 0.0),
     (14, 32, 402, 192, 2056, 2, 0.5),
     (24, 32, 700, 128, 520, 3, 0.9),
+    (12, 32, 384, 256, 33288, 1, 0.0),
+    (20, 32, 600, 320, 40000, 2, 0.5),
 ])
 def test_partials_match_sweep(gpu_lib, B1, N, M, D, V, k_max, tau):
     rng = np.random.default_rng(M * 7 + V)
