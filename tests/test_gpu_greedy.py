@@ -5,11 +5,12 @@ T = 0), through the C ABI.
 The sweep path is pinned to the oracle bit for bit on seeded host logits
 (test_gpu_parity); here the partials path must give the same logits (the same
 kernel arithmetic), the same tokens, committed positions and next states, and
-confidences within the fast path's bound, on shapes across the
-weight-streaming regime (129..256 rows, ragged vocabularies whose last tile
-is partly past V, two or more k-stages per tile), at the full SDAR-8B-like
-shape, with the threshold commit, and on planted exact and near ties that
-force the fp64 re-decision.  Properties of the outputs on their own logits are checked as
+confidences within the fast path's bound, on shapes served by both kernels
+that write partials (33..160 rows: the weight-streaming kernel, 128-id tiles;
+above: the large-tile kernel, 256-id tiles, mixed row-tile heights), ragged
+vocabularies whose last tile is partly past V, at the full SDAR-8B-like and
+D3D packed-tray shapes, with the threshold commit, and on planted exact and
+near ties that force the fp64 re-decision.  Properties of the outputs on their own logits are checked as
 well: each token is the row's first argmax, conf * sum exp(l - max) = 1
 within 1e-5, and each branch commits a position of maximal confidence."""
 import functools
@@ -200,5 +201,24 @@ def test_partials_match_sweep_full_shape(gpu_lib):
     _compare(a, b, x["state"], wl.N, 1)
     step = step_for(wl, x)
     assert step.fuse, "the benchmark's greedy step runs on the tile partials"
+    del xd, step
+    torch.cuda.empty_cache()
+
+
+def test_partials_match_sweep_packed_trays_shape(gpu_lib):
+    """The D3D-style packed workload (24 trays x 16, all masked: M = 384, D = 4096,
+    V = 151936), greedy: the large-tile LM head with two 192-row tiles writes the
+    partials, and both paths must agree."""
+    wl = synth.WORKLOADS[4]
+    x = synth.draw_inputs(wl)
+    xd = to_device(x)
+    M = int((x["state"] == sfv.SFV_MASK).sum())
+    assert M == 384
+    say(f"greedy partials at the packed-tray shape M={M}")
+    a, b = _run_both(xd["hidden"], xd["w"], xd["state"], [int(p) for p in x["parent"]], wl.B1, wl.N, M, wl.D,
+                     wl.V)
+    _compare(a, b, x["state"], wl.N, 1)
+    step = step_for(wl, x)
+    assert step.fuse, "the packed-tray greedy step runs on the tile partials"
     del xd, step
     torch.cuda.empty_cache()
