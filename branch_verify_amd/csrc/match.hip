@@ -6,14 +6,17 @@
 // the target accepts the longest prefix consistent with its own trajectory;
 // with shared noise that is state equality (Proposition 2).
 //
-// One workgroup of four waves.  Phase 1 spreads the (row, position) elements
-// of the 2*B1 rows (every drafted state and every next state) over all
-// threads, so their loads are issued together: each row's 64-bit hash is the
-// sum over positions of mix(n, token), order-free, so LDS atomic adds build
-// it; every draft position is checked against its parent's.
+// One workgroup of four waves.  Both state arrays and the first commit
+// position of every branch are first copied into LDS by all threads, so every
+// later step (and each hop of the walk, whose reads depend on the previous
+// hop) reads LDS rather than waiting on global memory.  Phase 1 spreads the
+// (row, position) elements of the 2*B1 rows (every drafted state and every
+// next state) over all threads: each row's 64-bit hash is the sum over
+// positions of mix(n, token), order-free, so LDS atomic adds build it; every
+// draft position is checked against its parent's.
 // Phase 2 is the walk, in wave 0: each hop ballots the drafts whose hash
-// equals the current next state and confirms the lowest candidate by a full,
-// coalesced comparison, so a hash collision can never produce a false match.
+// equals the current next state and confirms the lowest candidate by a full
+// comparison, so a hash collision can never produce a false match.
 #include "common.h"
 #include "internal.h"
 
@@ -39,9 +42,18 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
   __shared__ unsigned long long hn[kMaxBranches];  // hash of next_state[i]
   __shared__ int fresh[kMaxBranches];              // positions a draft unmasks over its parent
   __shared__ int bad_s;
+  __shared__ int ls[kMaxBranches * kMaxBlock];  // state, [B1][N]
+  __shared__ int ln[kMaxBranches * kMaxBlock];  // next_state, [B1][N]
+  __shared__ int lc[kMaxBranches];              // commit_pos[i][0]
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int B1 = tree.B1;
+  const int total = B1 * N;
+  for (int e = t; e < total; e += kThreads) {
+    ls[e] = state[e];
+    ln[e] = next_state[e];
+  }
   if (t < B1) {
+    lc[t] = commit_pos[t * k_max];
     hs[t] = 0ull;
     hn[t] = 0ull;
     fresh[t] = 0;
@@ -57,11 +69,11 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
     const int row = e / N, n = e % N;
     const bool is_next = row >= B1;
     const int i = is_next ? row - B1 : row;
-    const int v = (is_next ? next_state : state)[(size_t)i * N + n];
+    const int v = (is_next ? ln : ls)[i * N + n];
     atomicAdd(&(is_next ? hn : hs)[i], (unsigned long long)mix(((uint64_t)(uint32_t)n << 32) | (uint32_t)v));
     if (!is_next && S_max >= 0 && i >= 1) {
       // a draft keeps every unmasked token of its parent and unmasks at most S_max more
-      const int sp = state[(size_t)tree.parent[i] * N + n];
+      const int sp = ls[tree.parent[i] * N + n];
       if (sp != -1) {
         if (v != sp) bad_s = 1;
       } else if (v != -1) {
@@ -85,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
   const uint64_t my_hs = lane < B1 ? hs[lane] : 0ull;
   int cur = 0, h = 0;
   while (h < B1 - 1) {
-    if (commit_pos[cur * k_max] == -1) break;
+    if (lc[cur] == -1) break;
     const uint64_t target = hn[cur];
     unsigned long long cand = __ballot(lane >= 1 && lane < B1 && my_hs == target);
     int found = -1;
@@ -94,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
       cand &= cand - 1;
       bool diff = false;
       for (int n = lane; n < N; n += kWave)
-        diff = diff || (state[(size_t)j * N + n] != next_state[(size_t)cur * N + n]);
+        diff = diff || (ls[j * N + n] != ln[cur * N + n]);
       if (!__any(diff)) {
         found = j;
         break;

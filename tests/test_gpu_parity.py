@@ -394,6 +394,76 @@ def test_state_violation_status(gpu_lib):
     assert res["status"] == O.SFV_OK
 
 
+@pytest.mark.parametrize("hops,dup", [(40, True), (63, False), (0, False)])
+def test_match_largest_tree(gpu_lib, hops, dup):
+    """sfv_match_tree alone at 64 branches x 256 positions (the largest
+    supported tree and block): a planted chain of `hops` drafts, each the
+    committed next state of the one before, the others random one-position
+    extensions of a random parent; with `dup` one more draft repeats a chain
+    state at a higher index, and the lowest must be taken.  hops = 63 walks
+    every branch (the B-hop limit); hops = 0 plants nothing."""
+    rng = np.random.default_rng(1000 + hops)
+    B1, N, V = 64, 256, 1000
+    say(f"match largest tree hops={hops} dup={dup}")
+    chain = sorted(rng.choice(np.arange(1, B1), hops, replace=False).tolist())
+    on_chain = set(chain)
+    state = np.empty((B1, N), np.int32)
+    nxt = np.empty((B1, N), np.int32)
+    cpos = np.empty((B1, 1), np.int32)
+    parent = [-1] * B1
+    state[0] = rng.integers(0, V, N)
+    state[0, rng.random(N) < 0.7] = O.MASK
+    prev = 0
+    dup_at = None
+    for i in range(B1):
+        if i > 0:
+            if i in on_chain:
+                parent[i], state[i] = prev, nxt[prev]
+                prev = i
+            elif dup and dup_at is None and len([c for c in chain if c < i]) >= 5:
+                c5 = [c for c in chain if c < i][4]
+                parent[i], state[i] = parent[c5], state[c5]
+                dup_at = (i, c5)
+            else:
+                p = int(rng.integers(0, i))
+                parent[i], row = p, state[p].copy()
+                free = np.flatnonzero(row == O.MASK)
+                row[int(rng.choice(free))] = int(rng.integers(0, V))
+                state[i] = row
+        free = np.flatnonzero(state[i] == O.MASK)
+        n0 = int(rng.choice(free))
+        nxt[i] = state[i]
+        nxt[i, n0] = int(rng.integers(0, V))
+        cpos[i, 0] = n0
+    if dup:
+        assert dup_at is not None
+    st_d, nx_d, cp_d = (torch.from_numpy(a).cuda() for a in (state, nxt, cpos))
+    for S_max in (1, -1):
+        ch = torch.full((B1,), -9, dtype=torch.int32, device="cuda")
+        h = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+        status = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+        gpu_lib.sfv_match_tree(st_d, nx_d, cp_d, parent, B1, N, 1, S_max, ch, h, status)
+        torch.cuda.synchronize()
+        ref_chain, ref_h, ref_status = O.match_tree(state, nxt, cpos, np.array(parent), S_max=S_max)
+        assert int(status.item()) == ref_status == O.SFV_OK
+        assert int(h.item()) == ref_h == hops
+        assert np.array_equal(ch.cpu().numpy(), ref_chain)
+        assert ref_chain[:hops].tolist() == chain
+    # one changed token in a chain state's last position breaks the chain there
+    if hops:
+        bad = state.copy()
+        k = len(chain) // 2
+        bad[chain[k], N - 1] = (bad[chain[k], N - 1] + 1) % V if bad[chain[k], N - 1] >= 0 else 3
+        ch = torch.full((B1,), -9, dtype=torch.int32, device="cuda")
+        h = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+        status = torch.full((1,), -9, dtype=torch.int32, device="cuda")
+        gpu_lib.sfv_match_tree(torch.from_numpy(bad).cuda(), nx_d, cp_d, parent, B1, N, 1, -1, ch, h, status)
+        torch.cuda.synchronize()
+        ref_chain, ref_h, _ = O.match_tree(bad, nxt, cpos, np.array(parent), S_max=-1)
+        assert int(h.item()) == ref_h
+        assert np.array_equal(ch.cpu().numpy(), ref_chain)
+
+
 # ---------------------------------------------------------------------------
 # ragged and degenerate shapes
 # ---------------------------------------------------------------------------
