@@ -47,8 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the attention in order on the main stream instead of beside the LM head")
-    ap.add_argument("--attn-with", choices=["commit", "lm_head"], default="lm_head",
-                    help="start the overlapped attention after the LM head (beside the commit) or with it")
+    ap.add_argument("--attn-with", choices=["auto", "commit", "lm_head"], default="auto",
+                    help="start the overlapped attention after the LM head (beside the commit) or with "
+                         "it; auto: with the weight-streaming LM head, after the large-tile one")
     ap.add_argument("--no-graph", action="store_true",
                     help="issue the timed steps call by call instead of replaying a HIP graph")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -356,7 +357,8 @@ def main():
                    "temperature": wl.T, "parallelism": "none (1 GPU)",
                    "launch": "call by call" if a.no_graph else "hip graph",
                    "attention": "in order" if a.no_overlap else
-                   ("beside the commit" if a.attn_with == "commit" else "beside the LM head")},
+                   ("beside the commit" if step.attn_placement(a.attn_with) == "commit"
+                    else "beside the LM head")},
         "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "lm_head",
                      "achieved": achieved,
                      "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,

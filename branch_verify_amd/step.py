@@ -13,6 +13,10 @@ import torch
 
 from . import sfv
 
+# The weight-streaming LM head serves up to this many masked rows; above it the
+# large-tile kernel runs (libsfv picks the kernel by M with the same limit).
+STREAM_ROWS = 160
+
 
 def to_device(inp: dict, device="cuda") -> dict:
     """Host inputs from synth.draw_inputs -> device tensors (bf16 stays bf16)."""
@@ -113,17 +117,29 @@ class VerifyStep:
         sfv.sfv_match_tree(x["state"], self.next_state, self.commit_pos, self.parent, self.B1,
                            self.N, self.k_max, self.S_max, self.chain, self.n_accepted, self.status, stream)
 
-    def run(self, x, stream=None, overlap=True, attn_with="lm_head"):
+    def attn_placement(self, attn_with="auto"):
+        """Where the overlapped attention starts: "lm_head" (beside it) or
+        "commit" (after it, beside the commit and the walk).  "auto" picks by
+        the LM head's regime: up to STREAM_ROWS masked rows the weight-streaming
+        kernel runs two workgroups per CU and waits on memory, so the attention
+        shares the CUs with it; above, the large-tile kernel fills each CU's LDS
+        and the attention would only delay its tiles, so it goes beside the
+        commit instead."""
+        if attn_with == "auto":
+            return "lm_head" if self.M <= STREAM_ROWS else "commit"
+        if attn_with not in ("lm_head", "commit"):
+            raise ValueError(f"attn_with must be 'auto', 'lm_head' or 'commit', not {attn_with!r}")
+        return attn_with
+
+    def run(self, x, stream=None, overlap=True, attn_with="auto"):
         """The whole hot path, stream-ordered, no host synchronisation.
 
         Attention depends only on q/k/v, so with overlap=True it runs on a
         second stream, joined before the call returns; everything else stays
-        in order on `stream`.  attn_with="commit" starts it when the LM head
-        is done, beside the commit and the walk (the LM head keeps the whole
-        GPU); attn_with="lm_head" (the default, measured faster: the commit's
-        sweep also fills the GPU) starts it with the LM head.  Greedy steps in
-        the weight-streaming regime (with fuse) commit from the LM head's tile
-        partials."""
+        in order on `stream`.  Where it starts is attn_placement(attn_with).
+        Greedy steps in the LM head's tile-partial regime (with fuse) commit
+        from the partials."""
+        attn_with = self.attn_placement(attn_with)
         if not overlap:
             self.attend(x, stream)
             self.masked_rows(x, stream)
@@ -149,7 +165,7 @@ class VerifyStep:
         self._join.record(self._side)
         main.wait_event(self._join)
 
-    def capture(self, x, overlap=True, attn_with="lm_head"):
+    def capture(self, x, overlap=True, attn_with="auto"):
         """Capture one whole step (both streams) in a HIP graph; replay() then
         launches it with one call.  The graph holds the current buffers and
         inputs: replays recompute the same step."""
