@@ -46,10 +46,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true",
-                    help="run the attention in order on the main stream instead of beside the LM head")
-    ap.add_argument("--attn-with", choices=["auto", "commit", "lm_head"], default="auto",
-                    help="start the overlapped attention after the LM head (beside the commit) or with "
-                         "it; auto: with the weight-streaming LM head, after the large-tile one")
+                    help="run the attention in order on the main stream whatever --attn-with says")
+    ap.add_argument("--attn-with", choices=["auto", "in_order", "commit", "lm_head"], default="auto",
+                    help="run the attention first in order, or on a second stream beside the commit "
+                         "or beside the LM head; auto: in order unless it is long, then beside the commit")
     ap.add_argument("--no-graph", action="store_true",
                     help="issue the timed steps call by call instead of replaying a HIP graph")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -160,9 +160,9 @@ def main():
         step.run(xd)
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps (attention overlapped with the rest on a
-    # second stream, joined inside each step), replayed from a HIP graph of
-    # one step unless --no-graph, bracketed by synchronize.
+    # Timed region: K whole steps (the attention in order, or on a second
+    # stream joined inside each step, as --attn-with places it), replayed from
+    # a HIP graph of one step unless --no-graph, bracketed by synchronize.
     if not a.no_graph:
         step.capture(xd, overlap=not a.no_overlap, attn_with=a.attn_with)
         for _ in range(2):
@@ -357,8 +357,8 @@ def main():
                    "temperature": wl.T, "parallelism": "none (1 GPU)",
                    "launch": "call by call" if a.no_graph else "hip graph",
                    "attention": "in order" if a.no_overlap else
-                   ("beside the commit" if step.attn_placement(a.attn_with) == "commit"
-                    else "beside the LM head")},
+                   {"in_order": "in order", "commit": "beside the commit",
+                    "lm_head": "beside the LM head"}[step.attn_placement(a.attn_with)]},
         "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "lm_head",
                      "achieved": achieved,
                      "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,

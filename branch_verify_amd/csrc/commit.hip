@@ -142,7 +142,9 @@ __global__ __launch_bounds__(1024) void masked_rows_kernel(const int32_t* state,
 __global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* rows, int M, int N,
                                                                TreeArgs tree, bool noisy, WsLayout ws) {
   __shared__ int wsum[kThreads / kWave];
-  __shared__ int rowmap[kMaxBranches * kMaxBlock];  // flat position -> row, -1 if not masked
+  // flat position -> row, -1 if not masked: B1 * N ints, sized at launch so
+  // that the kernel fits beside long-running workgroups of other streams
+  extern __shared__ int rowmap[];
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   if (!noisy) {
     if (t == 0) *ws.count = M;
@@ -189,14 +191,18 @@ __global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* ro
     for (int a = tree.level_start[lv]; a < tree.level_start[lv + 1]; ++a) {
       const int r = rowmap[tree.by_level[a] * N + n];
       if (r < 0) continue;
-      it.rows[it.nrows++] = r;
-      if (it.nrows == kItemRows) {
+#pragma unroll
+      for (int k = 0; k < kItemRows; ++k)  // constant slot indices keep the item in registers
+        if (k == it.nrows) it.rows[k] = r;
+      if (++it.nrows == kItemRows) {
         ws.items[off++] = it;
         it.nrows = 0;
       }
     }
     if (it.nrows > 0) {
-      for (int k = it.nrows; k < kItemRows; ++k) it.rows[k] = -1;
+#pragma unroll
+      for (int k = 0; k < kItemRows; ++k)
+        if (k >= it.nrows) it.rows[k] = -1;
       ws.items[off++] = it;
     }
   }
@@ -915,7 +921,8 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
   WsLayout ws = ws_layout(ws_base, tree.B1, N, M, plan.items_max);
   hipError_t e = hipSuccess;
   if (noisy) {  // work items group the rows of equal (depth, position); at T = 0 an item is a row
-    hipLaunchKernelGGL(commit_plan_kernel, dim3(1), dim3(kThreads), 0, stream, rows, M, N, tree, noisy, ws);
+    const size_t lds = (size_t)tree.B1 * N * sizeof(int);  // at most 64 KB (64 branches x 256)
+    hipLaunchKernelGGL(commit_plan_kernel, dim3(1), dim3(kThreads), lds, stream, rows, M, N, tree, noisy, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -7,7 +7,8 @@
 // with shared noise that is state equality (Proposition 2).
 //
 // One workgroup of four waves.  Both state arrays and the first commit
-// position of every branch are first copied into LDS by all threads, so every
+// position of every branch are first copied into LDS by all threads (the
+// state arrays into launch-sized dynamic LDS), so every
 // later step (and each hop of the walk, whose reads depend on the previous
 // hop) reads LDS rather than waiting on global memory.  Phase 1 spreads the
 // (row, position) elements of the 2*B1 rows (every drafted state and every
@@ -42,12 +43,14 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
   __shared__ unsigned long long hn[kMaxBranches];  // hash of next_state[i]
   __shared__ int fresh[kMaxBranches];              // positions a draft unmasks over its parent
   __shared__ int bad_s;
-  __shared__ int ls[kMaxBranches * kMaxBlock];  // state, [B1][N]
-  __shared__ int ln[kMaxBranches * kMaxBlock];  // next_state, [B1][N]
-  __shared__ int lc[kMaxBranches];              // commit_pos[i][0]
+  __shared__ int lc[kMaxBranches];  // commit_pos[i][0]
+  // state then next_state, [B1][N] each, sized at launch (2 * B1 * N ints)
+  extern __shared__ int lstage[];
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int B1 = tree.B1;
   const int total = B1 * N;
+  int* ls = lstage;
+  int* ln = lstage + total;
   for (int e = t; e < total; e += kThreads) {
     ls[e] = state[e];
     ln[e] = next_state[e];
@@ -129,7 +132,16 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
 hipError_t launch_match(const int32_t* state, const int32_t* next_state, const int32_t* commit_pos,
                         const TreeArgs& tree, int N, int k_max, int S_max, int32_t* chain,
                         int32_t* n_accepted, int32_t* status, hipStream_t stream) {
-  hipLaunchKernelGGL(match_kernel, dim3(1), dim3(kThreads), 0, stream, state, next_state, commit_pos,
+  // Only the staged arrays are sized at launch: a small tree leaves room on a
+  // CU beside long-running workgroups of other streams.  Above 64 KB (up to
+  // 128 KB at 64 branches x 256 positions) the kernel's limit is raised first.
+  const size_t lds = 2 * (size_t)tree.B1 * N * sizeof(int);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&match_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(match_kernel, dim3(1), dim3(kThreads), lds, stream, state, next_state, commit_pos,
                      tree, N, k_max, S_max, chain, n_accepted, status);
   return hipGetLastError();
 }

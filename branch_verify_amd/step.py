@@ -13,9 +13,9 @@ import torch
 
 from . import sfv
 
-# The weight-streaming LM head serves up to this many masked rows; above it the
-# large-tile kernel runs (libsfv picks the kernel by M with the same limit).
-STREAM_ROWS = 160
+# Attention work (4 * rows * query heads * d * keys) from which the automatic
+# placement overlaps it with the commit instead of running it in order.
+ATTN_OVERLAP_FLOP = 50e9
 
 
 def to_device(inp: dict, device="cuda") -> dict:
@@ -118,29 +118,37 @@ class VerifyStep:
                            self.N, self.k_max, self.S_max, self.chain, self.n_accepted, self.status, stream)
 
     def attn_placement(self, attn_with="auto"):
-        """Where the overlapped attention starts: "lm_head" (beside it) or
-        "commit" (after it, beside the commit and the walk).  "auto" picks by
-        the LM head's regime: up to STREAM_ROWS masked rows the weight-streaming
-        kernel runs two workgroups per CU and waits on memory, so the attention
-        shares the CUs with it; above, the large-tile kernel fills each CU's LDS
-        and the attention would only delay its tiles, so it goes beside the
-        commit instead."""
+        """Where the attention runs: "in_order" (first, on the caller's
+        stream), "lm_head" (on a second stream, beside the LM head) or
+        "commit" (on a second stream once the LM head is done, beside the
+        commit and the walk).
+
+        Two workgroups of the attention fill a CU's registers, so a kernel on
+        the other stream shares the GPU with it only CU by CU: overlapping
+        pays where one of them leaves CUs idle, not otherwise.  "auto" runs a
+        short attention in order and overlaps one of at least
+        ATTN_OVERLAP_FLOP with the commit: the last round of its many
+        long-lived workgroups leaves most CUs idle, and the commit's sweep
+        fills them.  (Beside the large-tile LM head, which holds most of each
+        CU's LDS, the attention would only delay its tiles.)"""
         if attn_with == "auto":
-            return "lm_head" if self.M <= STREAM_ROWS else "commit"
-        if attn_with not in ("lm_head", "commit"):
-            raise ValueError(f"attn_with must be 'auto', 'lm_head' or 'commit', not {attn_with!r}")
+            flop = 4.0 * self.B1 * self.N * self.Hq * self.d * (self.L + self.N)
+            return "commit" if flop >= ATTN_OVERLAP_FLOP else "in_order"
+        if attn_with not in ("in_order", "lm_head", "commit"):
+            raise ValueError(f"attn_with must be 'auto', 'in_order', 'lm_head' or 'commit', not {attn_with!r}")
         return attn_with
 
     def run(self, x, stream=None, overlap=True, attn_with="auto"):
         """The whole hot path, stream-ordered, no host synchronisation.
 
-        Attention depends only on q/k/v, so with overlap=True it runs on a
+        Attention depends only on q/k/v, so with overlap=True it may run on a
         second stream, joined before the call returns; everything else stays
-        in order on `stream`.  Where it starts is attn_placement(attn_with).
+        in order on `stream`.  Where it runs is attn_placement(attn_with);
+        overlap=False runs it in order whatever attn_with says.
         Greedy steps in the LM head's tile-partial regime (with fuse) commit
         from the partials."""
         attn_with = self.attn_placement(attn_with)
-        if not overlap:
+        if not overlap or attn_with == "in_order":
             self.attend(x, stream)
             self.masked_rows(x, stream)
             self.head(x, stream)

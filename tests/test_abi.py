@@ -143,23 +143,24 @@ def test_greedy_partials_validation(lib):
     assert g(f, f, 148, 200, f, 128, 512, f, f, nb - 16, None) == sfv.SFV_E_WORKSPACE
 
 
-def test_step_row_limit_matches_library(lib):
-    """The step's placement of the attention keys on the same row limit at
-    which libsfv switches from the weight-streaming LM head (128-id tile
-    partials) to the large-tile one (256-id tiles)."""
+def test_step_attention_placement():
+    """The automatic attention placement of the workload shapes."""
     import types
 
-    from branch_verify_amd.step import STREAM_ROWS, VerifyStep
-    R = STREAM_ROWS
-    assert _ws(lib.sfv_lm_head_greedy_bytes, R, 1000, 128)[1] == 8 * R * 16
-    assert _ws(lib.sfv_lm_head_greedy_bytes, R + 1, 1000, 128)[1] == 4 * (R + 1) * 16
+    from branch_verify_amd.step import VerifyStep
     place = VerifyStep.attn_placement
-    assert place(types.SimpleNamespace(M=148)) == "lm_head"
-    assert place(types.SimpleNamespace(M=R)) == "lm_head"
-    assert place(types.SimpleNamespace(M=R + 1)) == "commit"
-    assert place(types.SimpleNamespace(M=1482), "lm_head") == "lm_head"
+
+    def shape(B1, N, L, Hq, d=128):
+        return types.SimpleNamespace(B1=B1, N=N, L=L, Hq=Hq, d=d, M=0)
+    # the SDAR-8B-like, D3D-style and Qwen3-32B-like steps: only the last one's
+    # attention (about 0.29 TFLOP) is long enough to overlap
+    assert place(shape(9, 32, 256, 32)) == "in_order"
+    assert place(shape(21, 32, 768, 32)) == "in_order"
+    assert place(shape(24, 16, 2048, 32)) == "in_order"
+    assert place(shape(33, 64, 4096, 64)) == "commit"
+    assert place(shape(9, 32, 256, 32), "lm_head") == "lm_head"
     with pytest.raises(ValueError):
-        place(types.SimpleNamespace(M=148), "beside")
+        place(shape(9, 32, 256, 32), "beside")
 
 
 def _commit_greedy(lib, parent, B1=9, N=32, M=148, V=512, D=128, k_max=1, tau=0.0, ws_bytes=None,

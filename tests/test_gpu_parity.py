@@ -227,20 +227,22 @@ def test_full_step_parity(gpu_lib, idx):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("attn_with", ["auto", "lm_head", "commit"])
 @pytest.mark.parametrize("idx", [2, 3])
-def test_graph_replay_matches_eager(gpu_lib, idx):
-    """The whole step captured in a HIP graph: every replay (with eager work and
-    synchronisation between replays, and the outputs overwritten before each)
-    reproduces the eager step bit for bit."""
+def test_graph_replay_matches_eager(gpu_lib, idx, attn_with):
+    """The whole step captured in a HIP graph, with the attention in order or
+    on a second stream beside the LM head or the commit: every replay (with
+    eager work and synchronisation between replays, and the outputs
+    overwritten before each) reproduces the eager in-order step bit for bit."""
     wl = synth.WORKLOADS[idx]
-    say(f"graph replay, workload {idx}")
+    say(f"graph replay, workload {idx}, attention {attn_with}")
     x = host_inputs(idx)
     xd = to_device(x)
     step = step_for(wl, x)
-    step.run(xd)
+    step.run(xd, overlap=False)
     ref = {k: (v.clone() if torch.is_tensor(v) else np.copy(v) if isinstance(v, np.ndarray) else v)
            for k, v in step.results().items()}
-    step.capture(xd)
+    step.capture(xd, attn_with=attn_with)
     outs = [step.o, step.lse, step.logits, step.next_state, step.commit_pos, step.token, step.conf,
             step.chain, step.n_accepted, step.status, step.rows, step.count]
     for rep in range(3):
