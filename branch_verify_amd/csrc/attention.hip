@@ -549,7 +549,9 @@ AttnPlan attn_plan(int B1, int N, int L, int Hq, int Hkv, int d) {
   int splits = 1;
   if (L > 0) {
     const int want = (512 + base - 1) / base;       // aim for >= 512 workgroups
-    const int most = L / 128 > 0 ? L / 128 : 1;     // at least 128 context keys per split
+    // at least 512 context keys per split: a shorter split's fixed costs (Q
+    // loads, the fp32 partial state, the merge) outweigh the parallelism
+    const int most = L / 512 > 0 ? L / 512 : 1;
     splits = want < most ? want : most;
     if (splits < 1) splits = 1;
     if (splits > 16) splits = 16;

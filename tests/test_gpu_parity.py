@@ -475,6 +475,8 @@ def test_match_largest_tree(gpu_lib, hops, dup):
     dict(B1=1, N=64, L=1000, Hq=16, Hkv=2, d=128),
     dict(B1=64, N=3, L=70, Hq=4, Hkv=4, d=128),
     dict(B1=3, N=256, L=130, Hq=2, Hkv=1, d=32),
+    dict(B1=2, N=5, L=1500, Hq=8, Hkv=2, d=64),   # 2 context splits, the last one ragged
+    dict(B1=3, N=9, L=3000, Hq=4, Hkv=4, d=32),   # 5 context splits, the last one ragged
 ])
 def test_attention_ragged(gpu_lib, shape):
     rng = np.random.default_rng(9)
