@@ -185,9 +185,9 @@ def check_commit_properties(x, res, wl):
 
 
 def run_twice(step, xd):
-    """The step overlapped (attention on a second stream), then in order on one
-    stream: every output must be bit-identical."""
-    step.run(xd)
+    """The step overlapped (attention on a second stream, beside the commit),
+    then in order on one stream: every output must be bit-identical."""
+    step.run(xd, attn_with="commit")
     first = step.results()
     snap = {k: (v.clone() if torch.is_tensor(v) else np.copy(v) if isinstance(v, np.ndarray) else v)
             for k, v in first.items()}
