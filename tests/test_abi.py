@@ -56,6 +56,25 @@ def test_attend_workspace_validation(lib):
     assert lib.sfv_attend_workspace_bytes(3, 8, 64, 4, 2, 32, None) == sfv.SFV_E_INVAL
 
 
+@pytest.mark.parametrize("B1,N,L,Hq,Hkv,d,splits", [
+    (9, 32, 256, 32, 8, 128, 1),      # SDAR-8B-like budget 8: one split, no partial state
+    (21, 32, 768, 32, 8, 128, 1),     # budget 20
+    (24, 16, 2048, 32, 8, 128, 4),    # D3D-style packed trays: 96 row tiles x heads, 512 keys a split
+    (33, 64, 4096, 64, 8, 128, 1),    # Qwen3-32B-like: 1056 workgroups without splitting
+    (2, 5, 1500, 8, 2, 64, 2),        # 750 keys rounded up to 768 a split: 2, the last ragged
+    (3, 9, 3000, 4, 4, 32, 5),        # 640 keys a split: 5
+    (1, 1, 511, 1, 1, 32, 1),         # below 512 keys: never split
+])
+def test_attend_split_plan(lib, B1, N, L, Hq, Hkv, d, splits):
+    """The split planner, seen through the workspace size: at least 512 context
+    keys per split, as many splits as bring the grid to 512 workgroups; one
+    split needs no workspace."""
+    rc, nb = _ws(lib.sfv_attend_workspace_bytes, B1, N, L, Hq, Hkv, d)
+    assert rc == sfv.SFV_OK
+    rows = B1 * N * (Hq // Hkv)
+    assert nb == (0 if splits == 1 else splits * Hkv * rows * (d + 2) * 4)
+
+
 def test_attend_rejects_before_launch(lib):
     P = ctypes.c_void_p
     fake = P(0x1000)
