@@ -127,7 +127,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the step is not "
-              "sharded across GPUs in this build", file=sys.stderr)
+              "sharded across GPUs", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
