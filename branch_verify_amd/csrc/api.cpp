@@ -119,7 +119,8 @@ int sfv_attend_branches(const void* q, const void* k_blk, const void* v_blk, con
   if (rc != SFV_OK) return rc;
   if (!q || !k_blk || !v_blk || !o || !lse) return fail(SFV_E_INVAL, "null tensor pointer");
   if (L > 0 && (!k_ctx || !v_ctx)) return fail(SFV_E_INVAL, "null context pointer with L=%d", L);
-  if (!std::isfinite(softmax_scale)) return fail(SFV_E_INVAL, "softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(SFV_E_INVAL, "softmax_scale=%g must be finite and > 0", (double)softmax_scale);
   const sfv::AttnPlan plan = sfv::attn_plan(B1, N, L, Hq, Hkv, d);
   if (workspace_bytes < plan.ws_bytes) {
     return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
@@ -219,7 +220,8 @@ int sfv_attend_folded(const void* q, const void* k_blk, const void* v_blk, const
   if (!q || !k_blk || !v_blk || !o || !lse || !src || !rec_rows || !rec_count || !rec_pos)
     return fail(SFV_E_INVAL, "null pointer");
   if (L > 0 && (!k_ctx || !v_ctx)) return fail(SFV_E_INVAL, "null context pointer with L=%d", L);
-  if (!std::isfinite(softmax_scale)) return fail(SFV_E_INVAL, "softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(SFV_E_INVAL, "softmax_scale=%g must be finite and > 0", (double)softmax_scale);
   const sfv::AttnPlan plan = sfv::attn_plan(B1, N, L, Hq, Hkv, d);
   if (workspace_bytes < plan.ws_bytes_folded) {
     return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes_folded);
@@ -241,7 +243,8 @@ int sfv_attend_trays(const void* q, const void* k_blk, const void* v_blk, const 
   if (rc != SFV_OK) return rc;
   if (!q || !k_blk || !v_blk || !o || !lse) return fail(SFV_E_INVAL, "null tensor pointer");
   if (L > 0 && (!k_ctx || !v_ctx)) return fail(SFV_E_INVAL, "null context pointer with L=%d", L);
-  if (!std::isfinite(softmax_scale)) return fail(SFV_E_INVAL, "softmax_scale is not finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(SFV_E_INVAL, "softmax_scale=%g must be finite and > 0", (double)softmax_scale);
   const sfv::AttnPlan plan = sfv::attn_plan(B1, N, L, Hq, Hkv, d);
   if (workspace_bytes < plan.ws_bytes) {
     return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);

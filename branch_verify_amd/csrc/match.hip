@@ -15,9 +15,14 @@
 // next state) over all threads: each row's 64-bit hash is the sum over
 // positions of mix(n, token), order-free, so LDS atomic adds build it; every
 // draft position is checked against its parent's.
-// Phase 2 is the walk, in wave 0: each hop ballots the drafts whose hash
-// equals the current next state and confirms the lowest candidate by a full
-// comparison, so a hash collision can never produce a false match.
+// Phase 2 is the walk, in wave 0: each hop ballots the drafts one tree level
+// below the current branch whose hash equals its next state and confirms the
+// lowest candidate by a full comparison, so a hash collision can never
+// produce a false match.  Only the next level counts: a draft at depth d
+// commits with the noise of step step0 + d, so one at another depth holding
+// the right state would continue the run with another step's noise and leave
+// the draft-free trajectory (SPOT, "Is the output exact when the target
+// samples?", Proposition 2).
 #include "common.h"
 #include "internal.h"
 
@@ -98,11 +103,13 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
     return;
   }
   const uint64_t my_hs = lane < B1 ? hs[lane] : 0ull;
-  int cur = 0, h = 0;
+  const int my_depth = lane < B1 ? (int)tree.depth[lane] : -1;
+  int cur = 0, h = 0, cur_depth = 0;
   while (h < B1 - 1) {
     if (lc[cur] == -1) break;
     const uint64_t target = hn[cur];
-    unsigned long long cand = __ballot(lane >= 1 && lane < B1 && my_hs == target);
+    unsigned long long cand =
+        __ballot(lane >= 1 && lane < B1 && my_depth == cur_depth + 1 && my_hs == target);
     int found = -1;
     while (cand) {
       const int j = __ffsll((long long)cand) - 1;
@@ -119,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void match_kernel(const int32_t* state, c
     if (lane == 0) chain[h] = found;
     ++h;
     cur = found;
+    ++cur_depth;
   }
   for (int j = h + lane; j < B1; j += kWave) chain[j] = -1;
   if (lane == 0) {

@@ -76,7 +76,9 @@ int sfv_version(void);
  *   o      [B1][N][Hq][d]  bf16 (round to nearest even)
  *   lse    [B1][N][Hq]     fp32
  * Supported: d in {32, 64, 128}; Hq/Hkv in {1, 2, 4, 8}; 1 <= B1 <= 64;
- * 1 <= N <= 256; L >= 0.  fp32 accumulation.
+ * 1 <= N <= 256; L >= 0.  fp32 accumulation.  softmax_scale must be finite
+ * and > 0 (the kernel tracks the running maximum of the unscaled scores), else
+ * SFV_E_INVAL; this holds for sfv_attend_trays and sfv_attend_folded too.
  * `workspace` holds split-context partial states; its size comes from
  * sfv_attend_workspace_bytes (may be 0, then workspace may be NULL).
  */
@@ -358,8 +360,14 @@ int sfv_commit_greedy(const void* partials, size_t partials_bytes, int D, const 
  * target's own trajectory).
  *
  * cur = 0; repeat at most B1-1 times: stop if commit_pos[cur][0] == -1;
- * j = lowest draft index >= 1 with state[j] == next_state[cur] (64-bit state
- * hash, confirmed by full comparison); stop if none; append j; cur = j.
+ * j = lowest draft index >= 1 with depth(j) == depth(cur) + 1 and
+ * state[j] == next_state[cur] (64-bit state hash, confirmed by full
+ * comparison); stop if none; append j; cur = j.  depth() is the distance to
+ * the root in parent_host.  Only the next tree level is searched because a
+ * draft at depth d commits with the noise of step step0 + d (sfv_commit): a
+ * draft at another depth would continue with another step's noise, and the
+ * accepted run would no longer be the draft-free trajectory (SPOT, "Is the
+ * output exact when the target samples?", Proposition 2).
  *   chain [B1] int32 out (-1 padded); n_accepted [1] int32 out (h)
  *   status [1] int32 out: SFV_OK, or SFV_E_STATE when S_max >= 0 and some
  *   draft changes or re-masks a parent position or unmasks more than S_max

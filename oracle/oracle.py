@@ -384,9 +384,16 @@ def match_tree(state, next_state, commit_pos, parent, S_max=-1):
     [SF] introduction: a later main-branch state that equals a cached draft
     reuses that draft's logits; [SPOT] "How does SPOT draft and verify?":
     accept the longest prefix consistent with the target's own trajectory.
-    From the main branch, repeatedly find the lowest draft index whose state
-    equals the current branch's committed next state, and move there.  Stops
-    on a miss, when the current branch had nothing to commit, or after B hops.
+    From the main branch, repeatedly find the lowest draft index, one tree
+    level below the current branch, whose state equals the current branch's
+    committed next state, and move there.  Stops on a miss, when the current
+    branch had nothing to commit, or after B hops.
+
+    The level condition: a draft at depth d stands for the trajectory's state
+    after d steps, and its own commit draws the noise of step step0 + d.  A
+    draft at another depth holding the right state would commit with another
+    step's noise, and the accepted run would leave the draft-free trajectory
+    ([SPOT] "Is the output exact when the target samples?", Proposition 2).
 
     With S_max >= 0 the drafts are first checked to extend their parent by at
     most S_max positions; a violation returns status SFV_E_STATE and accepts
@@ -398,11 +405,13 @@ def match_tree(state, next_state, commit_pos, parent, S_max=-1):
     chain = np.full(B1, -1, dtype=np.int32)
     if S_max >= 0 and state_violations(state, parent, S_max):
         return chain, 0, SFV_E_STATE
+    depth = tree_depths(parent)
     cur, h = 0, 0
     while h < B1 - 1:
         if commit_pos[cur, 0] == -1:
             break
-        hit = [j for j in range(1, B1) if np.array_equal(state[j], next_state[cur])]
+        hit = [j for j in range(1, B1)
+               if depth[j] == depth[cur] + 1 and np.array_equal(state[j], next_state[cur])]
         if not hit:
             break
         cur = hit[0]

@@ -90,9 +90,11 @@ def test_attend_rejects_before_launch(lib):
     assert need > 0
     args2 = [fake] * 5 + [9, 32, 4096, 32, 8, 128, ctypes.c_float(0.088), fake, fake]
     assert lib.sfv_attend_branches(*args2, fake, need - 1, None) == sfv.SFV_E_WORKSPACE
-    # non-finite scale
-    args3 = list(args); args3[11] = ctypes.c_float(float("inf"))
-    assert lib.sfv_attend_branches(*args3, fake, 1 << 30, None) == sfv.SFV_E_INVAL
+    # non-finite, zero or negative scale (the running max is of unscaled scores)
+    for bad_scale in (float("inf"), 0.0, -0.17, -0.0):
+        args3 = list(args); args3[11] = ctypes.c_float(bad_scale)
+        assert lib.sfv_attend_branches(*args3, fake, 1 << 30, None) == sfv.SFV_E_INVAL
+        assert lib.sfv_attend_trays(*args3, fake, 1 << 30, None) == sfv.SFV_E_INVAL
 
 
 def test_lm_head_validation(lib):
@@ -279,6 +281,8 @@ def test_attend_folded_validation(lib):
     assert call(d=96) == sfv.SFV_E_UNSUPPORTED
     assert call(G=(48, 3)) == sfv.SFV_E_UNSUPPORTED
     assert call(scale=float("nan")) == sfv.SFV_E_INVAL
+    assert call(scale=0.0) == sfv.SFV_E_INVAL
+    assert call(scale=-0.17) == sfv.SFV_E_INVAL
     assert call(o=P(0x1002)) == sfv.SFV_E_INVAL
     assert call(B1=0) == sfv.SFV_E_INVAL
     assert call(N=257) == sfv.SFV_E_INVAL

@@ -121,3 +121,90 @@ def test_inconsistent_draft_sets_status():
     assert O.match_tree(st, nxt, cpos, par, S_max=2)[1:] == (1, O.SFV_OK)
     chain, h, status = O.match_tree(st, nxt, cpos, par, S_max=1)
     assert status == O.SFV_E_STATE and h == 0 and list(chain) == [-1, -1]
+
+
+def _walk_by_levels(st, par, traj):
+    """Brute force of the accepted run length: the largest k such that every
+    tree level 1..k holds a draft equal to the draft-free state after that
+    many steps (the walk may jump between subtrees of one level), cut where a
+    trajectory state has nothing left to commit."""
+    depth = O.tree_depths(par)
+    k = 0
+    while k + 1 < len(traj) and np.any(O.masked_rows(traj[k][None]).size > 0):
+        level = [j for j in range(1, st.shape[0]) if depth[j] == k + 1]
+        if not any(np.array_equal(st[j], traj[k + 1]) for j in level):
+            break
+        k += 1
+    return k
+
+
+def _mixed_depth_tree(rng, traj, B1):
+    """Drafts hold draft-free states at any depth: a child copies its parent's
+    trajectory state (0 new positions) or moves 1 or 2 steps along it, so the
+    same state appears at depths other than its step count; a few drafts are
+    one-position decoys off the trajectory."""
+    st, par, t_of = [traj[0]], [-1], [0]
+    while len(st) < B1:
+        p = int(rng.integers(0, len(st)))
+        if t_of[p] < 0 or rng.random() < 0.2:
+            row = st[p].copy()
+            free = np.flatnonzero(row == O.MASK)
+            if free.size == 0:
+                continue
+            row[int(rng.choice(free))] = int(rng.integers(0, V))
+            if any(np.array_equal(row, s) for s in traj):
+                continue
+            st.append(row); par.append(p); t_of.append(-1)
+            continue
+        t = min(len(traj) - 1, t_of[p] + int(rng.integers(0, 3)))
+        st.append(traj[t].copy()); par.append(p); t_of.append(t)
+    return np.stack(st).astype(np.int32), np.array(par)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+@pytest.mark.parametrize("case", range(12))
+def test_mixed_depth_drafts_keep_the_draft_free_trajectory(T, case):
+    """States of the draft-free trajectory placed at the wrong tree depth (a
+    zero-position draft shifts its subtree down a level; a two-position draft
+    shifts it up) must not extend the run: the final state after the step
+    equals draft-free decoding for h + 1 steps (SPOT, Proposition 2 at
+    T = 1, Proposition 1 at T = 0), and h is the level-by-level brute force."""
+    rng = np.random.default_rng(700 + case)
+    s0 = rng.integers(0, V, N).astype(np.int32)
+    s0[rng.choice(N, 7, replace=False)] = O.MASK
+    step0, pos0 = 60 + case, 333
+    traj = _decode_free(s0, T, step0, pos0, 7)
+    st, par = _mixed_depth_tree(rng, traj, B1=int(rng.integers(6, 20)))
+    assert O.state_violations(st, par, 2) == []
+    rows = O.masked_rows(st)
+    logits = np.concatenate([synth.state_keyed_logits(SEED, st[i], V)[[r - i * N for r in rows if r // N == i]]
+                             for i in range(st.shape[0])])
+    nxt, cpos, tok, conf, S = O.commit(logits, rows, st, par, T, SEED, step0, pos0)
+    chain, h, status = O.match_tree(st, nxt, cpos, par, S_max=2)
+    assert status == O.SFV_OK
+    assert h == _walk_by_levels(st, par, traj)
+    depth = O.tree_depths(par)
+    assert [int(depth[j]) for j in chain[:h]] == list(range(1, h + 1))
+    longer = _decode_free(s0, T, step0, pos0, h + 1)
+    assert np.array_equal(O.final_state(nxt, chain, h), longer[-1])
+
+
+def test_two_position_draft_at_depth_one_is_not_a_second_hop():
+    """Main branch, its one-step draft-free successor at depth 1, and the
+    two-step successor also at depth 1 (it unmasks two positions).  The walk
+    takes one hop only: continuing from the depth-1 two-step state would
+    commit it with the noise of step step0 + 1 instead of step0 + 2."""
+    for seed_case in range(20):
+        rng = np.random.default_rng(900 + seed_case)
+        s0 = rng.integers(0, V, N).astype(np.int32)
+        s0[rng.choice(N, 5, replace=False)] = O.MASK
+        traj = _decode_free(s0, 1.0, 7, 50, 3)
+        st = np.stack([traj[0], traj[1], traj[2]]).astype(np.int32)
+        par = np.array([-1, 0, 0])
+        rows = O.masked_rows(st)
+        logits = np.concatenate([synth.state_keyed_logits(SEED, st[i], V)[[r - i * N for r in rows if r // N == i]]
+                                 for i in range(3)])
+        nxt, cpos, *_ = O.commit(logits, rows, st, par, 1.0, SEED, 7, 50)
+        chain, h, status = O.match_tree(st, nxt, cpos, par, S_max=2)
+        assert status == O.SFV_OK and h == 1 and list(chain) == [1, -1, -1]
+        assert np.array_equal(O.final_state(nxt, chain, h), traj[2])
