@@ -24,11 +24,10 @@ Readings (the pages name the two baselines but give no algorithm):
     (parent k-1).
   * Tree: the next-position distribution at a node u is the confidences of
     u's masked positions normalised over them; a child u+n has probability
-    P(u) * c_n / sum_{m masked in u} c_m, every step in fp64, the sum taken
-    as a pairwise tree over 256 leaves (leaf m = c_m if m is masked in u,
-    else 0): level by level, element 2j plus element 2j+1 (the pages fix no
-    order).  A node offers its W most confident masked positions as
-    children.  Nodes are added best-first: the highest
+    P(u) * c_n / sum_{m masked in u} c_m, every step in fp64, the sum being
+    the exact sum of the fp64 confidences rounded once (math.fsum), which
+    depends on no order (the pages fix none).  A node offers its W most
+    confident masked positions as children.  Nodes are added best-first: the highest
     probability candidate, ties to the lower parent index, then the lower
     position, until D drafts or no candidate remains.  W = 1 is the chain.
   * Drafted token of position n in a child of a node at depth d: T = 0, the
@@ -43,25 +42,16 @@ Pins (tests/test_oracle_draft.py): top-K against repeated first-argmax
 removal; chain = best-first tree with W = 1; with a state-independent toy
 target the T = 0 chain equals the target's own commit trajectory (oracle
 commit); with K = V the drafted T > 0 token equals the commit rule's token;
-tree order against brute-force enumeration on tiny blocks.
+tree order against brute-force enumeration on tiny blocks in exact rational
+arithmetic.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
 from .oracle import MASK, gumbel
-
-SUM_LEAVES = 256
-
-
-def pairwise_sum(leaves) -> float:
-    """Sum of fp64 leaves as a fixed pairwise tree: each level adds element
-    2j and element 2j+1 of the previous one."""
-    x = np.asarray(leaves, dtype=np.float64)
-    assert x.shape[0] & (x.shape[0] - 1) == 0
-    while x.shape[0] > 1:
-        x = x[0::2] + x[1::2]
-    return float(x[0])
 
 
 def stale_topk(logits_row, K: int):
@@ -117,9 +107,7 @@ def draft_tree(root, top_ids, top_logit, conf, D: int, W: int, T: float, seed: i
         masked_u = [n for n in range(N) if states[u][n] == MASK]
         if not masked_u:
             return
-        leaves = np.zeros(SUM_LEAVES)
-        leaves[masked_u] = conf[masked_u].astype(np.float64)
-        total = pairwise_sum(leaves)
+        total = math.fsum(float(conf[m]) for m in masked_u)
         ranked = [n for n in order if states[u][n] == MASK][:W]
         for n in ranked:
             cand.append(((prob[u] * float(conf[n])) / total, u, n))

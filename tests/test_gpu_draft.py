@@ -1,7 +1,19 @@
 """GPU parity of drafting from stale conditionals against the CPU oracle,
 through the C ABI: top-K ids and logits bit-exact; draft trees (parents,
-states, draft count) bit-exact on the same seeded inputs; and a drafted chain
-fully accepted by a state-independent target at T = 0 and T > 0."""
+states, draft count) equal to the oracle's on the same seeded inputs, or
+differing from it only where two best-first candidates' probabilities are
+within TIE_REL of each other; and a drafted chain fully accepted by a
+state-independent target at T = 0 and T > 0.
+
+TIE_REL.  The kernel sums a node's normaliser as a fixed pairwise fp64 tree
+over 256 leaves, the oracle as the exact sum rounded once (math.fsum).  Per
+tree level the two probabilities P(u) c_n / sum c_m then differ by at most
+(8 + 0.5 + 4) fp64 roundings (the pairwise levels, the rounding of the exact
+sum, a multiply and a divide on each side), so by at most 63 * 12.5 * 2^-53
+< 1e-13 relative at the deepest tree (63 drafts).  A best-first choice can
+therefore differ only between candidates within 2e-13 of each other; 1e-12
+is used."""
+import math
 import sys
 
 import numpy as np
@@ -90,6 +102,56 @@ def run_tree(root, ids, vals, conf, D, W, T, seed, step0, pos0):
     return parent.cpu().numpy(), states.cpu().numpy(), int(nd.item())
 
 
+TIE_REL = 1e-12
+
+
+def check_tree(root, ids, vals, conf, D, W, T, seed, step0, pos0, p, s, nd):
+    """The kernel's tree against the oracle's.  Equal: done.  Otherwise it is
+    replayed best-first with the oracle's probabilities: every node must be a
+    live candidate (a top-W masked position of its parent, by the oracle's
+    confidence order) within TIE_REL of the best live candidate, carry the
+    oracle's drafted token, and the tree must stop exactly when the oracle's
+    rule does.  Returns the number of steps that took a near-tied
+    candidate other than the oracle's."""
+    p_ref, s_ref, nd_ref = Dr.draft_tree(root, ids, vals, conf, D, W, T, seed, step0, pos0)
+    if nd == nd_ref and np.array_equal(p, p_ref) and np.array_equal(s, s_ref):
+        return 0
+    N = root.shape[0]
+    W1 = max(W, 1)
+    order = Dr.confidence_order(root, conf)
+    prob, depth, cand = {0: 1.0}, {0: 0}, {}
+
+    def offer(u):
+        masked = [m for m in range(N) if s[u][m] == O.MASK]
+        if not masked:
+            return
+        total = math.fsum(float(conf[m]) for m in masked)
+        for n in [n for n in order if s[u][n] == O.MASK][:W1]:
+            cand[(u, n)] = (prob[u] * float(conf[n])) / total
+
+    offer(0)
+    assert np.array_equal(s[0], root) and p[0] == -1
+    deviations = 0
+    for b in range(1, nd + 1):
+        u = int(p[b])
+        assert 0 <= u < b
+        diff = np.flatnonzero(s[b] != s[u])
+        assert diff.size == 1, b
+        n = int(diff[0])
+        assert (u, n) in cand, (b, u, n)
+        best_key = min(cand, key=lambda k: (-cand[k], k[0], k[1]))
+        assert cand[(u, n)] >= cand[best_key] * (1 - TIE_REL), (b, cand[(u, n)], cand[best_key])
+        deviations += (u, n) != best_key
+        assert s[b][n] == Dr.drafted_token(ids[n], vals[n], T, seed, step0 + depth[u], pos0 + n)
+        prob[b], depth[b] = cand.pop((u, n)), depth[u] + 1
+        offer(b)
+    assert nd == D or not cand
+    for b in range(nd + 1, D + 1):
+        assert p[b] == 0 and np.array_equal(s[b], root)
+    assert deviations > 0      # a differing tree must have taken some near-tied candidate
+    return deviations
+
+
 @pytest.mark.parametrize("N,V,K,D,W,T", [
     (32, 151936, 32, 8, 0, 0.0), (32, 151936, 32, 20, 4, 0.0), (32, 4096, 32, 20, 4, 1.0),
     (64, 2048, 16, 63, 16, 0.7), (8, 512, 8, 63, 3, 1.0), (256, 1024, 32, 63, 2, 0.0),
@@ -100,11 +162,9 @@ def test_draft_tree_parity(gpu_lib, N, V, K, D, W, T):
     root, ids, vals, conf = _tree_inputs(rng, N, V, K, 0.6)
     seed, step0, pos0 = 11, 200 + D, 4096
     say(f"draft tree N={N} K={K} D={D} W={W} T={T} masked={int((root == -1).sum())}")
-    p_ref, s_ref, nd_ref = Dr.draft_tree(root, ids, vals, conf, D, W, T, seed, step0, pos0)
     p, s, nd = run_tree(root, ids, vals, conf, D, W, T, seed, step0, pos0)
-    assert nd == nd_ref
-    assert np.array_equal(p, p_ref)
-    assert np.array_equal(s, s_ref)
+    dev = check_tree(root, ids, vals, conf, D, W, T, seed, step0, pos0, p, s, nd)
+    say(f"draft tree: {nd} drafts, {dev} near-tie choices differ from the oracle's")
 
 
 @pytest.mark.parametrize("T", [0.0, 1.0, 0.5])

@@ -10,9 +10,13 @@ that write partials (33..160 rows: the weight-streaming kernel, 128-id tiles;
 above: the large-tile kernel, 256-id tiles, mixed row-tile heights), ragged
 vocabularies whose last tile is partly past V, at the full SDAR-8B-like and
 D3D packed-tray shapes, with the threshold commit, and on planted exact and
-near ties that force the fp64 re-decision.  Properties of the outputs on their own logits are checked as
-well: each token is the row's first argmax, conf * sum exp(l - max) = 1
-within 1e-5, and each branch commits a position of maximal confidence."""
+near ties that force the fp64 re-decision.  On every case the pair's outputs
+are also held to the oracle (oracle.commit on the pair's own fp32 logits,
+copied to the host): tokens, committed positions and next states bit-exact,
+confidences within 1e-5 relative; and properties of the outputs on their own
+logits are checked: each token is the row's first argmax, conf * sum
+exp(l - max) = 1 within 1e-5, and each branch commits a position of maximal
+confidence."""
 import functools
 import sys
 
@@ -22,6 +26,7 @@ import torch
 
 from branch_verify_amd import sfv, synth
 from branch_verify_amd.step import step_for, to_device
+from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +83,26 @@ def _run_both(hd, wd, state_d, parent, B1, N, M, D, V, k_max=1, tau=0.0):
     return out
 
 
-def _compare(sweep, parts, state, N, k_max):
+def _against_oracle(res, state, parent, k_max, tau):
+    """The pair's outputs against oracle.commit on the pair's own fp32 logits
+    (T = 0): tokens, committed positions and next states bit-exact."""
+    lg_host = res["logits"].cpu().numpy()
+    rows = O.masked_rows(state)
+    assert np.array_equal(res["rows"], rows)
+    nxt, cpos, tok, conf, _ = O.commit(lg_host, rows, state, np.asarray(parent), 0.0, 0, 0, 0,
+                                       k_max=k_max, tau=tau)
+    assert np.array_equal(res["token"], tok), np.flatnonzero(res["token"] != tok)[:10]
+    assert np.array_equal(res["commit_pos"], cpos), np.flatnonzero(np.any(res["commit_pos"] != cpos, 1))[:10]
+    assert np.array_equal(res["next_state"], nxt)
+    if conf.size:
+        rel = np.max(np.abs(res["conf"].astype(np.float64) / conf.astype(np.float64) - 1.0))
+        assert rel <= 1e-5, rel
+    say("greedy pair equals the oracle commit on its own logits")
+
+
+def _compare(sweep, parts, state, N, k_max, parent=None, tau=0.0):
+    if parent is not None:
+        _against_oracle(parts, state, parent, k_max, tau)
     assert torch.equal(sweep["logits"], parts["logits"]), "the same kernel arithmetic must give the same logits"
     assert np.array_equal(sweep["token"], parts["token"])
     assert np.array_equal(sweep["commit_pos"], parts["commit_pos"])
@@ -138,7 +162,7 @@ def test_partials_match_sweep(gpu_lib, B1, N, M, D, V, k_max, tau):
     wd = torch.from_numpy(w).view(torch.bfloat16).cuda()
     sd = torch.from_numpy(state).cuda()
     a, b = _run_both(hd, wd, sd, parent, B1, N, M, D, V, k_max, tau)
-    _compare(a, b, state, N, k_max)
+    _compare(a, b, state, N, k_max, parent, tau)
     a2, b2 = _run_both(hd, wd, sd, parent, B1, N, M, D, V, k_max, tau)
     for k in ("token", "commit_pos", "next_state", "conf"):
         assert np.array_equal(b[k], b2[k]), f"{k} differs between two identical runs"
@@ -177,7 +201,7 @@ def test_planted_ties_take_the_lowest_position(gpu_lib):
     sd = torch.from_numpy(state).cuda()
     say(f"planted ties: {len(pairs)} branches")
     a, b = _run_both(hd, wd, sd, parent, B1, N, M, D, V)
-    _compare(a, b, state, N, 1)
+    _compare(a, b, state, N, 1, parent)
     for i, a_, b_, exact in pairs:
         if exact:
             assert b["commit_pos"][i, 0] == a_, (i, a_, b_, b["commit_pos"][i, 0])
@@ -198,7 +222,7 @@ def test_partials_match_sweep_full_shape(gpu_lib):
     say(f"greedy partials at the full shape M={M}")
     a, b = _run_both(xd["hidden"], xd["w"], xd["state"], [int(p) for p in x["parent"]], wl.B1, wl.N, M, wl.D,
                      wl.V)
-    _compare(a, b, x["state"], wl.N, 1)
+    _compare(a, b, x["state"], wl.N, 1, x["parent"])
     step = step_for(wl, x)
     assert step.fuse, "the benchmark's greedy step runs on the tile partials"
     del xd, step
@@ -217,7 +241,7 @@ def test_partials_match_sweep_packed_trays_shape(gpu_lib):
     say(f"greedy partials at the packed-tray shape M={M}")
     a, b = _run_both(xd["hidden"], xd["w"], xd["state"], [int(p) for p in x["parent"]], wl.B1, wl.N, M, wl.D,
                      wl.V)
-    _compare(a, b, x["state"], wl.N, 1)
+    _compare(a, b, x["state"], wl.N, 1, x["parent"])
     step = step_for(wl, x)
     assert step.fuse, "the packed-tray greedy step runs on the tile partials"
     del xd, step

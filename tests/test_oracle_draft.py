@@ -1,6 +1,8 @@
 """Pins of the drafting oracle (SPOT: stale conditionals, draft tree,
 coupled-noise match; SSD-style chain, BlockSpec-style confidence tree)."""
 import itertools
+import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -90,24 +92,25 @@ def test_drafted_token_is_the_commit_token_when_k_is_v():
 
 
 def _brute_tree_nodes(root, conf, W):
-    """Every node reachable by committing top-W positions, with its probability."""
+    """Every node reachable by committing top-W positions, with its
+    probability in exact rational arithmetic (fp32 confidences are exact
+    rationals), so no rounding of the normaliser enters the ranking."""
     N = len(root)
     order = Dr.confidence_order(root, conf)
+    cq = {n: Fraction(float(conf[n])) for n in range(N)}
     out = []
 
     def rec(path, P):
         masked = [n for n in range(N) if root[n] == O.MASK and n not in path]
         if not masked:
             return
-        leaves = np.zeros(Dr.SUM_LEAVES)
-        leaves[masked] = conf[masked].astype(np.float64)
-        total = Dr.pairwise_sum(leaves)
+        total = sum((cq[m] for m in masked), Fraction(0))
         for n in [n for n in order if n not in path][:W]:
-            p = (P * float(conf[n])) / total
+            p = P * cq[n] / total
             out.append((p, path + (n,)))
             rec(path + (n,), p)
 
-    rec((), 1.0)
+    rec((), Fraction(1))
     return out
 
 
@@ -135,17 +138,34 @@ def test_tree_is_the_most_probable_nodes(W):
         assert diff.size == 1 and states[parent[b]][diff[0]] == O.MASK
 
 
-def test_pairwise_sum():
-    """Exact on integers; zero leaves change nothing; the tree order is the
-    level-by-level pairing (checked on values where the order matters)."""
-    x = np.arange(256, dtype=np.float64)
-    assert Dr.pairwise_sum(x) == 255 * 256 / 2
-    y = np.zeros(256)
-    y[[3, 17, 200]] = [1.5, 2.25, -0.75]
-    assert Dr.pairwise_sum(y) == 3.0
-    z = np.zeros(4)
-    z[:] = [1e16, 1.0, -1e16, 1.0]
-    assert Dr.pairwise_sum(z) == (1e16 + 1.0) + (-1e16 + 1.0)
+def test_tree_probabilities_match_exact_rationals():
+    """Every drafted node's probability, recomputed along its root path in
+    exact rational arithmetic and rounded once, is within a few fp64 ulps per
+    level of the best-first order the oracle took: the oracle's normaliser is
+    the exact sum rounded once, so equal sets of confidences give equal
+    normalisers in any position order."""
+    rng = np.random.default_rng(31)
+    N, V, K = 12, 40, 4
+    root = rng.integers(0, V, N)
+    root[rng.choice(N, 9, replace=False)] = O.MASK
+    _, ids, vals, conf = _stale_inputs(rng, N, V, K)
+    conf[[1, 4, 7]] = conf[0]                       # equal confidences at several positions
+    parent, states, nd = Dr.draft_tree(root, ids, vals, conf, D=30, W=3, T=0.0, seed=0, step0=0, pos0=0)
+    exact = {0: Fraction(1)}
+    for b in range(1, nd + 1):
+        u = int(parent[b])
+        masked = [m for m in range(N) if states[u][m] == O.MASK]
+        n = int(np.flatnonzero(states[b] != states[u])[0])
+        exact[b] = exact[u] * Fraction(float(conf[n])) / sum((Fraction(float(conf[m])) for m in masked),
+                                                             Fraction(0))
+    # best-first: the exact probabilities never increase along the drafting order
+    # by more than the rounding of the oracle's fp64 path products allows
+    for b in range(2, nd + 1):
+        assert float(exact[b]) <= float(exact[b - 1]) * (1 + 1e-13)
+    # the fsum normaliser is order-free: a permuted position order sums the same
+    masked0 = [m for m in range(N) if root[m] == O.MASK]
+    vals0 = [float(conf[m]) for m in masked0]
+    assert math.fsum(vals0) == math.fsum(vals0[::-1]) == float(sum(Fraction(v) for v in vals0))
 
 
 def test_tree_padding_and_probabilities_decrease():
