@@ -4,16 +4,24 @@ A step is the whole hot path over one batch: shared-prefix attention of every
 branch, masked-row scan, LM head over the masked rows, commit, and the
 draft-tree match, with all inputs resident in HBM.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 5] [--secondary 2]
+                    [--no-cpu-baseline] [--flush-mall]
+
+The headline workload is the largest single-GPU configuration, the
+Qwen3-32B-like wide step (33 branches x 64, context 4096, T = 1); the
+SDAR-8B-like budget-8 step is timed the same way and reported as a secondary
+object of the same line.
 
 value = B1*N branch-tokens verified per step / seconds per step, over K steps
-replayed from a HIP graph of one step, in which the attention (independent of
-the rest) runs on a second stream.  A
-second pass of K steps issued in order on one stream times each call with HIP
-events on the stream it runs on; the roofline object reports the dominant
-kernel (the LM head) from those against its binding peak (HBM bytes, or bf16
-MFMA FLOP when those take longer), with the HBM traffic its byte counters
-measured on this workload.  cpu_baseline times the CPU oracle on this host.
+replayed from a HIP graph of one step (the attention runs in order, or on a
+second stream beside the commit when it is long).  A second pass of K steps
+issued in order on one stream times each call with HIP events on the stream
+it runs on; the roofline object reports the dominant kernel (the LM head) from
+those against its binding peak (HBM bytes, or bf16 MFMA FLOP when those take
+longer), with the HBM traffic its byte counters measured on this workload.
+With --flush-mall a 512 MiB buffer is overwritten before every step of that
+pass (outside the events), so the per-kernel times start from a cold
+last-level cache.  cpu_baseline times the CPU oracle on this host.
 """
 from __future__ import annotations
 
@@ -31,7 +39,8 @@ sys.path.insert(0, ROOT)
 METRIC = "verified branch-tokens/s per verify step; % HBM peak (attn) and % MFMA peak (LM head)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lm_head_sdar8b_budget8_counters.md")
+PROFILES = os.path.join(ROOT, "profiles")
+MALL_FLUSH_BYTES = 512 << 20   # twice the 256 MB last-level cache
 
 
 def note(msg):
@@ -43,8 +52,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--secondary", type=int, default=2,
+                    help="a second workload timed the same way (graph replay and per-kernel events) "
+                         "and reported inside the line; 0 for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="overwrite a 512 MiB buffer before every step of the per-kernel event pass")
+    ap.add_argument("--no-side-legs", action="store_true",
+                    help="time only the step (no threshold, folded, drafting or tray legs)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the attention in order on the main stream whatever --attn-with says")
     ap.add_argument("--attn-with", choices=["auto", "in_order", "commit", "lm_head"], default="auto",
@@ -84,25 +100,26 @@ def source_digest(paths):
 
 
 def measured_traffic(workload):
-    """HBM bytes per LM-head launch from the committed counter summary, or None
-    when the counters were taken on another workload or the kernel source
-    changed since."""
-    if not os.path.exists(PROFILE_TRAFFIC):
-        return None
-    text = open(PROFILE_TRAFFIC).read()
-    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    s = re.search(r"lm_head_source_sha256_16:\s*([0-9a-f]+)", text)
-    w = re.search(r"traffic_workload:\s*(\S+)", text)
-    if not m or not s or not w or w.group(1) != workload:
-        return None
+    """HBM bytes per LM-head launch from a committed counter summary
+    (profiles/lm_head_*_counters.md) taken on this workload, or None when
+    there is none or the kernel source changed since the counters were taken."""
     here = source_digest(LM_HEAD_SOURCES)
-    return float(m.group(1)) if s.group(1) == here else None
+    for name in sorted(os.listdir(PROFILES)):
+        if not (name.startswith("lm_head_") and name.endswith("_counters.md")):
+            continue
+        text = open(os.path.join(PROFILES, name)).read()
+        m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+        s = re.search(r"lm_head_source_sha256_16:\s*([0-9a-f]+)", text)
+        w = re.search(r"traffic_workload:\s*(\S+)", text)
+        if m and s and w and w.group(1) == workload and s.group(1) == here:
+            return float(m.group(1))
+    return None
 
 
-def cpu_baseline(wl, x):
-    """The CPU oracle over the same workload (one full step), on this host."""
+def _oracle_steps(wl, x, budget_s, max_steps):
+    """Full oracle steps of one workload until about budget_s seconds of CPU
+    work; returns the per-step wall times."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from branch_verify_amd import synth
     from oracle import oracle as O
@@ -110,52 +127,65 @@ def cpu_baseline(wl, x):
     args = [f(x[k]) for k in ("q", "k_blk", "v_blk", "k_ctx", "v_ctx", "hidden")]
     w = f(x["w"])
     times = []
-    while len(times) < 10 and sum(times) < 10.0:   # about 10 s of CPU work
+    while len(times) < max_steps and (not times or sum(times) < budget_s):
         t0 = time.perf_counter()
         O.verify_step(*args, w, x["state"], x["parent"], wl.T, wl.seed, wl.step0, wl.pos0,
                       1.0 / np.sqrt(wl.d), S_max=wl.S_t)
         times.append(time.perf_counter() - t0)
+    return times
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, x, single_wl=None, single_x=None):
+    """The CPU oracle over the same workload (full steps, about 10-30 s of CPU
+    work), with numpy's BLAS on every core this process may use; and, when
+    single_wl is given, one full step of that (smaller) workload with BLAS
+    limited to one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] + [1])
+    blas = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('threading_layer', '?')})"
+                     for p in pools if p.get("user_api") == "blas") or "none found"
+    times = _oracle_steps(wl, x, 10.0, 10)
     dt = float(np.median(times))
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": wl.B1 * wl.N / dt, "unit": "branch-tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(times)} full verify steps of {wl.name} (fp64 numpy oracle), "
-                      f"median {dt:.2f} s per step"}
+    out = {"value": wl.B1 * wl.N / dt, "unit": "branch-tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{len(times)} full verify step(s) of {wl.name} (fp64 numpy oracle: attention, "
+                     f"LM head, commit, match), median {dt:.2f} s per step",
+           "cpu_model": _cpu_model(), "blas": blas,
+           "affinity_cores": len(os.sched_getaffinity(0))}
+    if single_wl is not None:
+        with threadpool_limits(limits=1):
+            t1 = _oracle_steps(single_wl, single_x, 0.0, 1)
+        out["single_thread"] = {"workload": single_wl.name, "value": single_wl.B1 * single_wl.N / t1[0],
+                                "unit": "branch-tokens/s", "cores": 1, "s_per_step": t1[0]}
+    return out
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the step is not "
-              "sharded across GPUs", file=sys.stderr)
-        sys.exit(2)
+def measure_step(wl, x, a, note_prefix=""):
+    """Warm-up, the timed graph replays, and the per-kernel event pass of one
+    workload's step.  Returns (step, device inputs, timing dict)."""
     import numpy as np
     import torch
 
-    from branch_verify_amd import synth
     from branch_verify_amd.step import step_for, to_device
 
-    wl = synth.WORKLOADS[a.workload]
-    note(f"drawing inputs of {wl.name}")
-    x = synth.draw_inputs(wl)
-    M = synth.masked_count(x["state"])
-    if a.cpu_only:
-        print(json.dumps(cpu_baseline(wl, x)))
-        return
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     xd = to_device(x)
     step = step_for(wl, x)
     stream = torch.cuda.current_stream()
-
-    if a.copy_bytes > 0:
-        note(f"calibration: 3 device copies of {a.copy_bytes} bytes")
-        src = torch.empty(a.copy_bytes, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    note(f"{a.warmup} warm-up steps, then {a.steps} timed steps")
+    note(f"{note_prefix}{a.warmup} warm-up steps, then {a.steps} timed steps")
     for _ in range(a.warmup):
         step.run(xd)
     torch.cuda.synchronize()
@@ -183,18 +213,135 @@ def main():
     calls = [step.attend, step.masked_rows, step.head, step.commit_step, step.match]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in names] for _ in range(a.steps)]
+    flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda") if a.flush_mall else None
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for s in range(a.steps):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
         for j, fn in enumerate(calls):
             ev[s][j][0].record(stream)
             fn(xd)
             ev[s][j][1].record(stream)
     torch.cuda.synchronize()
     elapsed_seq = time.perf_counter() - t1
-
+    del flush
     per = {n: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(a.steps)])) * 1e3
            for j, n in enumerate(names)}  # microseconds
+    M = step.M
+    alg = algorithmic(wl, M)
+    lm_bytes, lm_flop = alg["lm_head"]
+    lm_s = per["lm_head"] * 1e-6
+    # the LM head's binding roofline: HBM bytes or bf16 MFMA FLOP, whichever
+    # takes longer at its peak
+    mfma_bound = lm_flop / (BF16_PEAK_TFLOPS * 1e12) > lm_bytes / (HBM_PEAK_GBS * 1e9)
+    achieved = lm_flop / lm_s / 1e12 if mfma_bound else lm_bytes / lm_s / 1e9
+    out = {
+        "value": wl.B1 * wl.N / (elapsed / a.steps),
+        "ms_per_step": elapsed / a.steps * 1e3,
+        "config": {"workload": wl.name, "B1": wl.B1, "N": wl.N, "L": wl.L, "Hq": wl.Hq,
+                   "Hkv": wl.Hkv, "d": wl.d, "D": wl.D, "V": wl.V, "masked_rows": M,
+                   "temperature": wl.T, "parallelism": "none (1 GPU)",
+                   "launch": "call by call" if a.no_graph else "hip graph",
+                   "attention": "in order" if a.no_overlap else
+                   {"in_order": "in order", "commit": "beside the commit",
+                    "lm_head": "beside the LM head"}[step.attn_placement(a.attn_with)],
+                   "per_kernel_cache": "cold (512 MiB overwritten before each step)" if a.flush_mall
+                   else "warm"},
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "lm_head",
+                     "achieved": achieved,
+                     "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+                     "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                     "frac": achieved / (BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS),
+                     "traffic": measured_traffic(wl.name),
+                     "algorithmic_bytes": lm_bytes, "algorithmic_flop": lm_flop,
+                     "hbm_frac": lm_bytes / lm_s / 1e9 / HBM_PEAK_GBS,
+                     "mfma_frac": lm_flop / lm_s / 1e12 / BF16_PEAK_TFLOPS},
+        "kernels_us": per,
+        "ms_per_step_sequential": elapsed_seq / a.steps * 1e3,
+    }
+    ab, af = alg["attention"]
+    out["attention_roofline"] = {"hbm_frac": ab / (per["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                 "mfma_frac": af / (per["attention"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
+    cb, _ = alg["commit"]
+    if step.fuse:  # the commit reads the LM head's tile partials, not the logits
+        cb = cb - 4 * M * wl.V + step.parts_bytes
+    out["commit_roofline"] = {"hbm_frac": cb / (per["commit"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                              "reads": "tile partials" if step.fuse else "logits"}
+    return step, xd, out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the step is not "
+              "sharded across GPUs", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from branch_verify_amd import synth
+    from branch_verify_amd.step import step_for, to_device
+
+    wl = synth.WORKLOADS[a.workload]
+    sec_wl = synth.WORKLOADS[a.secondary] if a.secondary and a.secondary != a.workload else None
+    note(f"drawing inputs of {wl.name}")
+    x = synth.draw_inputs(wl)
+    M = synth.masked_count(x["state"])
+    if a.cpu_only:
+        sx = synth.draw_inputs(sec_wl) if sec_wl is not None else None
+        print(json.dumps(cpu_baseline(wl, x, sec_wl, sx)))
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    stream = torch.cuda.current_stream()
+
+    if a.copy_bytes > 0:
+        note(f"calibration: 3 device copies of {a.copy_bytes} bytes")
+        src = torch.empty(a.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # the secondary workload first, then the headline one (whose buffers the
+    # side legs below reuse)
+    secondary, sx = None, None
+    if sec_wl is not None:
+        note(f"secondary workload {sec_wl.name}")
+        sx = synth.draw_inputs(sec_wl)
+        s_step, s_xd, secondary = measure_step(sec_wl, sx, a, note_prefix=f"{sec_wl.name}: ")
+        del s_step, s_xd
+        torch.cuda.empty_cache()
+
+    step, xd, head = measure_step(wl, x, a, note_prefix=f"{wl.name}: ")
+    per = head["kernels_us"]
+    out = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "branch-tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    out.update({k: v for k, v in head.items() if k not in ("value", "ms_per_step")})
+    if secondary is not None:
+        out["secondary"] = secondary
+    if a.no_side_legs:
+        if not a.no_cpu_baseline:
+            note("timing the CPU oracle")
+        out["cpu_baseline"] = None if a.no_cpu_baseline else cpu_baseline(wl, x, sec_wl, sx)
+        print(json.dumps(out))
+        return
+    cb, _ = algorithmic(wl, M)["commit"]
+    if step.fuse:  # the commit reads the LM head's tile partials, not the logits
+        cb = cb - 4 * M * wl.V + step.parts_bytes
 
     # The threshold variant of the commit (up to k_max positions with
     # confidence >= 0.9 per branch), on the same logits, timed the same way.
@@ -330,54 +477,6 @@ def main():
     tray_accepted = tr_na.cpu().numpy()
     reject_bytes = 2 * 4 * n_tr * (B_tr + 1) * wl.V + 4 * n_tr * wl.V * 2   # two passes per row + emitting rows
     del tl, tq, tt, rj_ws, ta_q, ta_k, ta_v, ta_o, ta_lse, ta_ws
-    ms_per_step = elapsed / a.steps * 1e3
-    alg = algorithmic(wl, M)
-    lm_bytes, lm_flop = alg["lm_head"]
-    lm_s = per["lm_head"] * 1e-6
-    # the LM head's binding roofline: HBM bytes or bf16 MFMA FLOP, whichever
-    # takes longer at its peak
-    mfma_bound = lm_flop / (BF16_PEAK_TFLOPS * 1e12) > lm_bytes / (HBM_PEAK_GBS * 1e9)
-    achieved = lm_flop / lm_s / 1e12 if mfma_bound else lm_bytes / lm_s / 1e9
-    traffic = measured_traffic(wl.name)
-    out = {
-        "metric": METRIC,
-        "value": wl.B1 * wl.N / (elapsed / a.steps),
-        "unit": "branch-tokens/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "B1": wl.B1, "N": wl.N, "L": wl.L, "Hq": wl.Hq,
-                   "Hkv": wl.Hkv, "d": wl.d, "D": wl.D, "V": wl.V, "masked_rows": M,
-                   "temperature": wl.T, "parallelism": "none (1 GPU)",
-                   "launch": "call by call" if a.no_graph else "hip graph",
-                   "attention": "in order" if a.no_overlap else
-                   {"in_order": "in order", "commit": "beside the commit",
-                    "lm_head": "beside the LM head"}[step.attn_placement(a.attn_with)]},
-        "roofline": {"bound": "mfma" if mfma_bound else "hbm", "kernel": "lm_head",
-                     "achieved": achieved,
-                     "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
-                     "unit": "TFLOP/s" if mfma_bound else "GB/s",
-                     "frac": achieved / (BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS),
-                     "traffic": traffic,
-                     "hbm_frac": lm_bytes / lm_s / 1e9 / HBM_PEAK_GBS,
-                     "mfma_frac": lm_flop / lm_s / 1e12 / BF16_PEAK_TFLOPS},
-        "kernels_us": per,
-        "ms_per_step_sequential": elapsed_seq / a.steps * 1e3,
-    }
-    ab, af = alg["attention"]
-    out["attention_roofline"] = {"hbm_frac": ab / (per["attention"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                 "mfma_frac": af / (per["attention"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
-    cb, _ = alg["commit"]
-    if step.fuse:  # the commit reads the LM head's tile partials, not the logits
-        cb = cb - 4 * M * wl.V + step.parts_bytes
-    out["commit_roofline"] = {"hbm_frac": cb / (per["commit"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                              "reads": "tile partials" if step.fuse else "logits"}
     out["folded_attention"] = {"delta": fold_delta, "fold_ratio": fold_ratio, "gate_us": gate_us,
                                "attention_us": fattn_us, "dense_attention_us": per["attention"],
                                "speedup_vs_dense": per["attention"] / (gate_us + fattn_us),
@@ -393,7 +492,7 @@ def main():
                                "hbm_frac": cb / (thr_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
     if not a.no_cpu_baseline:
         note("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(wl, x)
+        out["cpu_baseline"] = cpu_baseline(wl, x, sec_wl, sx)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))
