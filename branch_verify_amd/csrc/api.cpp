@@ -342,14 +342,19 @@ int sfv_commit_workspace_bytes(int B1, int N, int M, int V, size_t* bytes) {
   return ok();
 }
 
-int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
-               const int32_t* parent_host, int B1, int N, int V, float temperature, uint64_t seed,
-               uint64_t step0, int64_t pos0, int k_max, float tau, int32_t* next_state,
-               int32_t* commit_pos, int32_t* token, float* conf, void* workspace,
-               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by sfv_commit and sfv_commit_noalloc; fills the tree
+// and the launch plan (whose ws_bytes is the workspace this call needs).
+int prepare_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
+                   const int32_t* parent_host, int B1, int N, int V, float temperature, int k_max,
+                   float tau, int32_t* next_state, int32_t* commit_pos, int32_t* token, float* conf,
+                   sfv::TreeArgs* tree, sfv::CommitPlan* plan) {
   int rc = check_commit_dims(B1, N, M, V);
   if (rc != SFV_OK) return rc;
-  if (!state || !next_state || !commit_pos || !workspace) return fail(SFV_E_INVAL, "null pointer");
+  if (!state || !next_state || !commit_pos) return fail(SFV_E_INVAL, "null pointer");
   if (M > 0 && (!logits || !rows || !token || !conf)) return fail(SFV_E_INVAL, "null pointer");
   if (!(temperature >= 0.f) || !std::isfinite(temperature)) {
     return fail(SFV_E_INVAL, "temperature must be finite and >= 0");
@@ -358,12 +363,29 @@ int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* s
   if (k_max > N) return fail(SFV_E_INVAL, "k_max=%d > N=%d", k_max, N);
   if (k_max > 1 && !std::isfinite(tau)) return fail(SFV_E_INVAL, "tau must be finite");
   if ((uintptr_t)logits % 16 != 0) return fail(SFV_E_INVAL, "logits must be 16-byte aligned");
-  sfv::TreeArgs tree;
-  rc = make_tree(parent_host, B1, &tree);
+  rc = make_tree(parent_host, B1, tree);
   if (rc != SFV_OK) return rc;
   const bool noisy = temperature > 0.f;
-  const int items = commit_items_max(tree, N, M, noisy);
-  const sfv::CommitPlan plan = sfv::commit_plan(B1, N, M, V, items, noisy);
+  const int items = commit_items_max(*tree, N, M, noisy);
+  *plan = sfv::commit_plan(B1, N, M, V, items, noisy);
+  return SFV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* state,
+               const int32_t* parent_host, int B1, int N, int V, float temperature, uint64_t seed,
+               uint64_t step0, int64_t pos0, int k_max, float tau, int32_t* next_state,
+               int32_t* commit_pos, int32_t* token, float* conf, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  sfv::TreeArgs tree;
+  sfv::CommitPlan plan;
+  const int rc = prepare_commit(logits, rows, M, state, parent_host, B1, N, V, temperature, k_max, tau,
+                                next_state, commit_pos, token, conf, &tree, &plan);
+  if (rc != SFV_OK) return rc;
+  if (!workspace) return fail(SFV_E_INVAL, "null pointer");
   if (workspace_bytes < plan.ws_bytes) {
     return fail(SFV_E_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
   }
@@ -372,6 +394,37 @@ int sfv_commit(const float* logits, const int32_t* rows, int M, const int32_t* s
                                        workspace, plan,
                                        (hipStream_t)stream),
                     "sfv_commit");
+}
+
+int sfv_commit_noalloc(const float* logits, const int32_t* rows, int M, const int32_t* state,
+                       const int32_t* parent_host, int B1, int N, int V, float temperature, uint64_t seed,
+                       uint64_t step0, int64_t pos0, int k_max, float tau, int32_t* next_state,
+                       int32_t* commit_pos, int32_t* token, float* conf, void* stream) {
+  sfv::TreeArgs tree;
+  sfv::CommitPlan plan;
+  const int rc = prepare_commit(logits, rows, M, state, parent_host, B1, N, V, temperature, k_max, tau,
+                                next_state, commit_pos, token, conf, &tree, &plan);
+  if (rc != SFV_OK) return rc;
+  if (plan.ws_bytes > sfv::kCommitScratchBytes) {
+    return fail(SFV_E_WORKSPACE, "this call needs %zu bytes of workspace; the static one holds %zu",
+                plan.ws_bytes, sfv::kCommitScratchBytes);
+  }
+  if (stream != nullptr) {
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return hip_status(e, "sfv_commit_noalloc");
+    if (sdev != cur) {
+      return fail(SFV_E_INVAL, "stream is on device %d, the current device is %d", sdev, cur);
+    }
+  }
+  void* ws = nullptr;
+  const hipError_t e = sfv::commit_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "sfv_commit_noalloc: static workspace address");
+  return hip_status(sfv::launch_commit(logits, rows, M, state, tree, N, V, temperature, seed, step0,
+                                       pos0, k_max, tau, next_state, commit_pos, token, conf, ws, plan,
+                                       (hipStream_t)stream),
+                    "sfv_commit_noalloc");
 }
 
 int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes) {

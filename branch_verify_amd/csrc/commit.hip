@@ -21,6 +21,8 @@
 //    bound E on |S - S_exact|.  A branch whose best and runner-up intervals
 //    [S - E, S + E] overlap is re-decided from S summed with fp64 exp.
 // This translation unit is compiled with -ffp-contract=off.
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 #include "noise.h"
@@ -903,6 +905,33 @@ CommitPlan commit_plan(int B1, int N, int M, int V, int items_max, bool noisy) {
   pl.chunk = chunk;
   pl.ws_bytes = ws_bytes(B1, N, M, items_max, splits);
   return pl;
+}
+
+// Workspace of sfv_commit_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  In host code `scratch` only names the
+// symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kCommitScratchBytes];
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+hipError_t commit_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t* count,

@@ -96,6 +96,11 @@ hipError_t launch_commit(const float* logits, const int32_t* rows, int M, const 
                          int32_t* token, float* conf, void* ws, const CommitPlan& plan,
                          hipStream_t stream);
 
+// Device address, on the current GPU, of the static workspace that
+// sfv_commit_noalloc uses in place of a caller's (kCommitScratchBytes).
+constexpr size_t kCommitScratchBytes = 1u << 20;
+hipError_t commit_scratch(void** ptr);
+
 // Greedy commit from the fused LM head's tile partials: a merge kernel
 // reduces the partials of every row to kGreedyChunks, then the commit's
 // finalize kernel (the same one the vocabulary sweep feeds) decides.

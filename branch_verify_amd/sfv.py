@@ -26,7 +26,7 @@ EXPORTS = [
     "sfv_attend_folded", "sfv_stale_topk_workspace_bytes", "sfv_stale_topk", "sfv_draft_tree",
     "sfv_attend_trays", "sfv_reject_workspace_bytes", "sfv_reject_verify", "sfv_match_trays",
     "sfv_lm_head_greedy_bytes", "sfv_lm_head_greedy", "sfv_commit_greedy_workspace_bytes",
-    "sfv_commit_greedy",
+    "sfv_commit_greedy", "sfv_commit_noalloc",
 ]
 
 _lib = None
@@ -69,6 +69,7 @@ def load(path: str = LIB_PATH):
     lib.sfv_lm_head.argtypes = [P, P, I, I, P, I, I, P, P]
     lib.sfv_commit_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_commit.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P, SZ, P]
+    lib.sfv_commit_noalloc.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P]
     lib.sfv_match_tree.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
     lib.sfv_lm_head_greedy_bytes.argtypes = [I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_lm_head_greedy.argtypes = [P, P, I, I, P, I, I, P, P, SZ, P]
@@ -166,6 +167,15 @@ def sfv_commit(logits, rows, M, state, parent_host, B1, N, V, temperature, seed,
         float(temperature), int(seed) & (2**64 - 1), int(step0) & (2**64 - 1), int(pos0), k_max,
         float(tau), _ptr(next_state), _ptr(commit_pos), _ptr(token), _ptr(conf), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
+
+
+def sfv_commit_noalloc(logits, rows, M, state, parent_host, B1, N, V, temperature, seed, step0, pos0,
+                       k_max, tau, next_state, commit_pos, token, conf, stream=None):
+    par = _host_i32(parent_host)
+    return _check(load().sfv_commit_noalloc(
+        _ptr(logits), _ptr(rows), M, _ptr(state), ctypes.cast(par, ctypes.c_void_p), B1, N, V,
+        float(temperature), int(seed) & (2**64 - 1), int(step0) & (2**64 - 1), int(pos0), k_max,
+        float(tau), _ptr(next_state), _ptr(commit_pos), _ptr(token), _ptr(conf), _stream(stream)))
 
 
 def sfv_lm_head_greedy_bytes(M, V, D) -> int:

@@ -319,6 +319,32 @@ int sfv_commit(const float* logits, const int32_t* rows, int M,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sfv_commit without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments (minus workspace and
+ * workspace_bytes), checks and outputs as sfv_commit; it runs the same
+ * kernels.  It calls no hipMalloc, hipFree or allocating library routine.
+ *
+ * The workspace is a static device array of SFV_COMMIT_SCRATCH_BYTES per GPU
+ * that the library holds until the process ends; its address on a GPU is
+ * looked up on the first call there.  A call whose workspace need (at most
+ * sfv_commit_workspace_bytes(B1, N, M, V); about 0.2 MB at 33 branches x 64
+ * positions with 1482 masked rows) exceeds it returns SFV_E_WORKSPACE before
+ * launching anything.  Every call on one GPU uses that one array, and each
+ * call writes what it reads, so nothing carries over between calls; but calls
+ * whose executions overlap on one GPU (on different streams, or unordered
+ * from several threads) race on it and give undefined results.  `stream`
+ * must be NULL or a stream of the current device (else SFV_E_INVAL).
+ */
+#define SFV_COMMIT_SCRATCH_BYTES (1u << 20)
+int sfv_commit_noalloc(const float* logits, const int32_t* rows, int M,
+                       const int32_t* state, const int32_t* parent_host,
+                       int B1, int N, int V, float temperature,
+                       uint64_t seed, uint64_t step0, int64_t pos0, int k_max, float tau,
+                       int32_t* next_state, int32_t* commit_pos, int32_t* token, float* conf,
+                       void* stream);
+
+/*
  * Greedy (T = 0) LM head and commit over tile partials: sfv_lm_head_greedy
  * then sfv_commit_greedy give the outputs of sfv_lm_head then sfv_commit at
  * temperature 0 (the same logits, tokens, committed positions and next

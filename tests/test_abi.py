@@ -365,3 +365,24 @@ def test_attend_trays_validation(lib):
     assert lib.sfv_attend_trays(None, *args[1:], None, 0, None) == sfv.SFV_E_INVAL
     bad = list(args); bad[10] = 96
     assert lib.sfv_attend_trays(*bad, None, 0, None) == sfv.SFV_E_UNSUPPORTED
+
+
+def test_commit_noalloc_limits(lib):
+    """The static-workspace commit checks its arguments as sfv_commit does and
+    rejects, before any device call, a shape whose workspace exceeds the
+    static array (64 x 256 positions all masked at T = 0 need 1048832 bytes)."""
+    P = ctypes.c_void_p
+    f = P(0x1000)
+
+    def call(parent, B1=3, N=8, M=4, V=512, T=0.0, k_max=1):
+        par = (ctypes.c_int32 * len(parent))(*parent)
+        return lib.sfv_commit_noalloc(f, f, M, f, ctypes.cast(par, P), B1, N, V, ctypes.c_float(T),
+                                      ctypes.c_uint64(1), ctypes.c_uint64(2), ctypes.c_int64(3), k_max,
+                                      ctypes.c_float(0.0), f, f, f, f, None)
+
+    assert call([0, 0, 1]) == sfv.SFV_E_TREE
+    assert call([-1, 0, 1], V=500) == sfv.SFV_E_UNSUPPORTED
+    assert call([-1, 0, 1], k_max=0) == sfv.SFV_E_INVAL
+    big = [-1] + [0] * 63
+    assert call(big, B1=64, N=256, M=64 * 256, V=151936) == sfv.SFV_E_WORKSPACE
+    assert b"static" in lib.sfv_last_error()
