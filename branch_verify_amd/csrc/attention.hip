@@ -41,7 +41,11 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kRows = 128;     // query rows per workgroup, 32 per wave
 constexpr int kKeys = 64;      // keys per LDS tile
-constexpr int kPad = 8;        // bf16 elements of row padding in LDS
+constexpr int kPad = 8;        // bf16 elements of row padding of the key tiles in LDS
+// Row padding of the transposed value tiles: a row is 34 dwords, so the
+// 8-byte reads of 32 consecutive rows (one per lane) fall on 32 distinct bank
+// pairs; with 36 dwords they met in pairs (two-way bank conflicts).
+constexpr int kVPad = 4;
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -72,7 +76,7 @@ struct Params {
 template <int D>
 struct Smem {
   unsigned short k[2][kKeys][D + kPad];   // key tiles, row-major (double buffered)
-  unsigned short vt[2][D][kKeys + kPad];  // value tiles, transposed
+  unsigned short vt[2][D][kKeys + kVPad];  // value tiles, transposed
 };
 
 // Which keys tile j of this workgroup covers: the context tiles of its split,
