@@ -312,7 +312,7 @@ int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t*
 }
 
 int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R, const void* w, int D, int V,
-                float* logits, void* stream) {
+                float* logits, int32_t* status, void* stream) {
   if (M < 0) return fail(SFV_E_INVAL, "M=%d < 0", M);
   if (R < 1) return fail(SFV_E_INVAL, "R=%d < 1", R);
   if (D < 1 || V < 1) return fail(SFV_E_INVAL, "D=%d, V=%d must be positive", D, V);
@@ -321,6 +321,11 @@ int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R, const voi
   if (M > 0 && (!hidden || !rows || !w || !logits)) return fail(SFV_E_INVAL, "null tensor pointer");
   const uintptr_t al = (uintptr_t)hidden | (uintptr_t)w | (uintptr_t)logits;
   if (al % 16 != 0) return fail(SFV_E_INVAL, "tensor pointers must be 16-byte aligned");
+  if ((uintptr_t)status % 4 != 0) return fail(SFV_E_INVAL, "status must be 4-byte aligned");
+  if (status) {
+    const hipError_t e = sfv::launch_rows_status(rows, M, R, status, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "sfv_lm_head: row check");
+  }
   return hip_status(sfv::launch_lm_head(hidden, rows, M, R, w, D, V, logits, (hipStream_t)stream),
                     "sfv_lm_head");
 }
@@ -440,7 +445,7 @@ int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes) {
 }
 
 int sfv_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w, int D, int V,
-                       float* logits, void* partials, size_t partials_bytes, void* stream) {
+                       float* logits, void* partials, size_t partials_bytes, int32_t* status, void* stream) {
   size_t need = 0;
   int rc = sfv_lm_head_greedy_bytes(M, V, D, &need);
   if (rc != SFV_OK) return rc;
@@ -450,6 +455,11 @@ int sfv_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, co
   const uintptr_t al = (uintptr_t)hidden | (uintptr_t)w | (uintptr_t)logits | (uintptr_t)partials;
   if (al % 16 != 0) return fail(SFV_E_INVAL, "tensor pointers must be 16-byte aligned");
   if (partials_bytes < need) return fail(SFV_E_WORKSPACE, "partials %zu bytes < %zu needed", partials_bytes, need);
+  if ((uintptr_t)status % 4 != 0) return fail(SFV_E_INVAL, "status must be 4-byte aligned");
+  if (status) {
+    const hipError_t e = sfv::launch_rows_status(rows, M, R, status, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "sfv_lm_head_greedy: row check");
+  }
   return hip_status(sfv::launch_lm_head_greedy(hidden, rows, M, R, w, D, V, logits,
                                                (sfv::GreedyPart*)partials, (hipStream_t)stream),
                     "sfv_lm_head_greedy");
@@ -508,6 +518,15 @@ int sfv_match_tree(const int32_t* state, const int32_t* next_state, const int32_
   return hip_status(sfv::launch_match(state, next_state, commit_pos, tree, N, k_max, S_max, chain,
                                       n_accepted, status, (hipStream_t)stream),
                     "sfv_match_tree");
+}
+
+int sfv_gumbel_words(uint32_t first, uint32_t count, float* out, void* stream) {
+  if (!out && count > 0) return fail(SFV_E_INVAL, "out is NULL");
+  if ((uintptr_t)out % 4 != 0) return fail(SFV_E_INVAL, "out must be 4-byte aligned");
+  if ((uint64_t)first + count > (1ull << 32)) {
+    return fail(SFV_E_INVAL, "words %u + %u run past 2^32", first, count);
+  }
+  return hip_status(sfv::launch_gumbel_words(first, count, out, (hipStream_t)stream), "sfv_gumbel_words");
 }
 
 int sfv_selfcheck_bounds(double* out, void* stream) {

@@ -867,6 +867,14 @@ __global__ __launch_bounds__(256) void selfcheck_gumbel_kernel(double* out) {
   if (threadIdx.x % kWave == 0) atomic_max_pos_double(out, worst);
 }
 
+// gumbel_exact of the words first .. first + count - 1 (the defined noise
+// value the commit's exact path uses), one per thread, grid-stride.
+__global__ __launch_bounds__(256) void gumbel_words_kernel(uint32_t first, uint32_t count, float* out) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+    out[i] = gumbel_exact(first + (uint32_t)i);
+}
+
 __global__ __launch_bounds__(256) void selfcheck_exp2_kernel(double* out) {
   // every fp32 x in [-126, 0]: bit patterns 0x80000000 .. 0xC2FC0000
   const uint64_t first = 0x80000000ull, last = 0xC2FC0000ull;
@@ -1027,6 +1035,14 @@ hipError_t launch_commit_greedy(const GreedyPart* gpart, int nparts, const float
   fa.tau = tau;
   fa.noisy = false;
   hipLaunchKernelGGL(commit_finalize_kernel, dim3(tree.B1), dim3(kThreads), 0, stream, fa, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_gumbel_words(uint32_t first, uint32_t count, float* out, hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  const uint64_t blocks = ((uint64_t)count + 255) / 256;
+  hipLaunchKernelGGL(gumbel_words_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream,
+                     first, count, out);
   return hipGetLastError();
 }
 

@@ -37,6 +37,9 @@ hipError_t launch_masked_rows(const int32_t* state, int B1, int N, int32_t* rows
 hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R, const void* w,
                           int D, int V, float* logits, hipStream_t stream);
 
+// *status = -1 (SFV_E_INVAL) if any of rows[0 .. M) lies outside [0, R), else 0.
+hipError_t launch_rows_status(const int32_t* rows, int M, int R, int32_t* status, hipStream_t stream);
+
 // Error model of a fast confidence term t = exp2(fl32(fl32(x - m) * log2e))
 // against exp(x - m), for a = m - x >= 0:  |t / exp(x - m) - 1| <= kExpC1 * a +
 // kExpC2.  kExpC1 covers the two fp32 roundings of the argument, kExpC2 the
@@ -116,6 +119,7 @@ hipError_t launch_match(const int32_t* state, const int32_t* next_state, const i
                         int32_t* n_accepted, int32_t* status, hipStream_t stream);
 
 hipError_t launch_selfcheck(double* out, hipStream_t stream);
+hipError_t launch_gumbel_words(uint32_t first, uint32_t count, float* out, hipStream_t stream);
 
 constexpr int kMaxTopk = 32;            // stale conditionals per position
 constexpr int kMaxTopkChunks = 16;      // workgroups per row of the stale top-K

@@ -726,12 +726,33 @@ hipError_t launch_big8(const Params& p0, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// One workgroup checks every row id: *status = -1 (SFV_E_INVAL) when some
+// id is outside [0, R), else 0.
+__global__ __launch_bounds__(256) void rows_status_kernel(const int32_t* rows, int M, int R, int32_t* status) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int m = threadIdx.x; m < M; m += 256) {
+    const int r = rows[m];
+    mine |= (r < 0 || r >= R);
+  }
+  if (__any(mine) && threadIdx.x % kWave == 0) bad = 1;  // (racing writes of the same value)
+  __syncthreads();
+  if (threadIdx.x == 0) *status = bad ? -1 : 0;
+}
+
 hipError_t launch_tiled(const Params& p, hipStream_t stream) {
   hipLaunchKernelGGL(lm_head_tiled, dim3(p.vt * p.mt), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_rows_status(const int32_t* rows, int M, int R, int32_t* status, hipStream_t stream) {
+  hipLaunchKernelGGL(rows_status_kernel, dim3(1), dim3(256), 0, stream, rows, M, R, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R, const void* w,
                           int D, int V, float* logits, hipStream_t stream) {

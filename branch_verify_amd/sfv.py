@@ -26,7 +26,7 @@ EXPORTS = [
     "sfv_attend_folded", "sfv_stale_topk_workspace_bytes", "sfv_stale_topk", "sfv_draft_tree",
     "sfv_attend_trays", "sfv_reject_workspace_bytes", "sfv_reject_verify", "sfv_match_trays",
     "sfv_lm_head_greedy_bytes", "sfv_lm_head_greedy", "sfv_commit_greedy_workspace_bytes",
-    "sfv_commit_greedy", "sfv_commit_noalloc",
+    "sfv_commit_greedy", "sfv_commit_noalloc", "sfv_gumbel_words",
 ]
 
 _lib = None
@@ -66,16 +66,17 @@ def load(path: str = LIB_PATH):
     lib.sfv_reject_verify.argtypes = [P, P, P, I, I, I, F, U64, U64, I64, P, P, P, SZ, P]
     lib.sfv_match_trays.argtypes = [P, P, I, P, P, I, P, P]
     lib.sfv_attend_trays.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, SZ, P]
-    lib.sfv_lm_head.argtypes = [P, P, I, I, P, I, I, P, P]
+    lib.sfv_lm_head.argtypes = [P, P, I, I, P, I, I, P, P, P]
     lib.sfv_commit_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_commit.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P, SZ, P]
     lib.sfv_commit_noalloc.argtypes = [P, P, I, P, P, I, I, I, F, U64, U64, I64, I, F, P, P, P, P, P]
     lib.sfv_match_tree.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
     lib.sfv_lm_head_greedy_bytes.argtypes = [I, I, I, ctypes.POINTER(SZ)]
-    lib.sfv_lm_head_greedy.argtypes = [P, P, I, I, P, I, I, P, P, SZ, P]
+    lib.sfv_lm_head_greedy.argtypes = [P, P, I, I, P, I, I, P, P, SZ, P, P]
     lib.sfv_commit_greedy_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_commit_greedy.argtypes = [P, SZ, I, P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, SZ, P]
     lib.sfv_selfcheck_bounds.argtypes = [P, P]
+    lib.sfv_gumbel_words.argtypes = [ctypes.c_uint32, ctypes.c_uint32, P, P]
     lib.sfv_stale_topk_workspace_bytes.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
     lib.sfv_stale_topk.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, SZ, P]
     lib.sfv_draft_tree.argtypes = [P, P, P, P, I, I, I, I, F, U64, U64, I64, P, P, P, P]
@@ -142,9 +143,9 @@ def sfv_masked_rows(state, B1, N, rows, count, stream=None):
     return _check(load().sfv_masked_rows(_ptr(state), B1, N, _ptr(rows), _ptr(count), _stream(stream)))
 
 
-def sfv_lm_head(hidden, rows, M, R, w, D, V, logits, stream=None):
+def sfv_lm_head(hidden, rows, M, R, w, D, V, logits, stream=None, status=None):
     return _check(load().sfv_lm_head(_ptr(hidden), _ptr(rows), M, R, _ptr(w), D, V, _ptr(logits),
-                                     _stream(stream)))
+                                     _ptr(status), _stream(stream)))
 
 
 def sfv_commit_workspace_bytes(B1, N, M, V) -> int:
@@ -189,9 +190,10 @@ def sfv_lm_head_greedy_bytes(M, V, D) -> int:
     return out.value
 
 
-def sfv_lm_head_greedy(hidden, rows, M, R, w, D, V, logits, partials, partials_bytes, stream=None):
+def sfv_lm_head_greedy(hidden, rows, M, R, w, D, V, logits, partials, partials_bytes, stream=None,
+                       status=None):
     return _check(load().sfv_lm_head_greedy(_ptr(hidden), _ptr(rows), M, R, _ptr(w), D, V, _ptr(logits),
-                                            _ptr(partials), int(partials_bytes), _stream(stream)))
+                                            _ptr(partials), int(partials_bytes), _ptr(status), _stream(stream)))
 
 
 def sfv_commit_greedy_workspace_bytes(B1, N, M, V) -> int:
@@ -215,6 +217,10 @@ def sfv_match_tree(state, next_state, commit_pos, parent_host, B1, N, k_max, S_m
     return _check(load().sfv_match_tree(
         _ptr(state), _ptr(next_state), _ptr(commit_pos), ctypes.cast(par, ctypes.c_void_p), B1, N,
         k_max, S_max, _ptr(chain), _ptr(n_accepted), _ptr(status), _stream(stream)))
+
+
+def sfv_gumbel_words(first, count, out, stream=None):
+    return _check(load().sfv_gumbel_words(int(first), int(count), _ptr(out), _stream(stream)))
 
 
 def sfv_selfcheck_bounds(out, stream=None):

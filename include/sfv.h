@@ -267,15 +267,17 @@ int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t*
  * head is a plain dense product): logits[r][v] = sum_k hidden[rows[r]][k] * w[v][k].
  *   hidden [R][D] bf16 (R = B1*N, rows index it); rows [M] int32, each in [0, R)
  *   w      [V][D] bf16;  logits [M][V] fp32 (fp32 accumulation)
- * Supported: D % 64 == 0, 1 <= V, 0 <= M.  Row ids should lie in [0, R); the
- * kernels clamp any outside it into that range (no error is reported), so a
- * bad id yields that clamped row's logits but never an access outside hidden.
- * Kernel by M: up to 32 rows a tiled kernel, 33..160 a weight-streaming kernel
+ * Supported: D % 64 == 0, 1 <= V, 0 <= M.  Row ids must lie in [0, R).  The
+ * kernels read an id outside it as the nearest id inside it (never an access
+ * outside hidden), so such a row's logits are another row's.  To detect them,
+ * pass `status` (device int32, or NULL): before the product a one-workgroup
+ * scan of rows writes *status = SFV_E_INVAL if any id is outside [0, R), else
+ * SFV_OK.  Kernel by M: up to 32 rows a tiled kernel, 33..160 a weight-streaming kernel
  * (the weight read from HBM once past every row), above that 256-id vocab
  * tiles of 256 or 192 rows.
  */
 int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R,
-                const void* w, int D, int V, float* logits, void* stream);
+                const void* w, int D, int V, float* logits, int32_t* status, void* stream);
 
 /*
  * Commit of every branch: token per masked row, confidence, unmask-argmax.
@@ -353,7 +355,7 @@ int sfv_commit_noalloc(const float* logits, const int32_t* rows, int M,
  * masked rows); SPOT, "Important context" (at T = 0 the commit is the greedy
  * argmax).
  *
- * sfv_lm_head_greedy: as sfv_lm_head, and the kernel also reduces every
+ * sfv_lm_head_greedy: as sfv_lm_head (status included), and the kernel also reduces every
  * vocabulary tile of every row (128 ids up to 160 rows, 256 ids above) to its
  * max, the lowest id attaining it and a fast fp32 sum of exp(l - max) with a
  * bound on its error.
@@ -372,7 +374,7 @@ int sfv_commit_noalloc(const float* logits, const int32_t* rows, int M,
  */
 int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes);
 int sfv_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w, int D, int V,
-                       float* logits, void* partials, size_t partials_bytes, void* stream);
+                       float* logits, void* partials, size_t partials_bytes, int32_t* status, void* stream);
 int sfv_commit_greedy_workspace_bytes(int B1, int N, int M, int V, size_t* bytes);
 int sfv_commit_greedy(const void* partials, size_t partials_bytes, int D, const float* logits,
                       const int32_t* rows, int M, const int32_t* state, const int32_t* parent_host, int B1,
@@ -412,6 +414,18 @@ int sfv_match_tree(const int32_t* state, const int32_t* next_state, const int32_
  *   out [2] fp64 device.  Synchronous on `stream`'s work only.
  */
 int sfv_selfcheck_bounds(double* out, void* stream);
+
+/*
+ * The Gumbel noise value of noise words, as the commit's exact path computes
+ * it: out[i] = fl32(-ln(-ln u)) with u = (w + 1/2) 2^-32, w = first + i, both
+ * logarithms in fp64 (SPOT, "Is the output exact when the target samples?":
+ * the drafter and the target must draw the same noise, Proposition 2).  For
+ * checking the device's values against an independent implementation, word by
+ * word.
+ *   out [count] fp32 device, 4-byte aligned.  first + count <= 2^32, else
+ *   SFV_E_INVAL.  count = 0 launches nothing.
+ */
+int sfv_gumbel_words(uint32_t first, uint32_t count, float* out, void* stream);
 
 #ifdef __cplusplus
 }

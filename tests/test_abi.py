@@ -100,11 +100,12 @@ def test_attend_rejects_before_launch(lib):
 def test_lm_head_validation(lib):
     P = ctypes.c_void_p
     f = P(0x1000)
-    assert lib.sfv_lm_head(f, f, -1, 8, f, 128, 512, f, None) == sfv.SFV_E_INVAL
-    assert lib.sfv_lm_head(f, f, 4, 8, f, 100, 512, f, None) == sfv.SFV_E_UNSUPPORTED
-    assert lib.sfv_lm_head(None, f, 4, 8, f, 128, 512, f, None) == sfv.SFV_E_INVAL
-    assert lib.sfv_lm_head(f, f, 4, 0, f, 128, 512, f, None) == sfv.SFV_E_INVAL
-    assert lib.sfv_lm_head(P(0x1004), f, 4, 8, f, 128, 512, f, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head(f, f, -1, 8, f, 128, 512, f, None, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head(f, f, 4, 8, f, 100, 512, f, None, None) == sfv.SFV_E_UNSUPPORTED
+    assert lib.sfv_lm_head(None, f, 4, 8, f, 128, 512, f, None, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head(f, f, 4, 0, f, 128, 512, f, None, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_lm_head(P(0x1004), f, 4, 8, f, 128, 512, f, None, None)
+    assert lib.sfv_lm_head(f, f, 4, 8, f, 128, 512, f, P(0x1002), None) == sfv.SFV_E_INVAL  # misaligned status == sfv.SFV_E_INVAL
 
 
 def _commit(lib, parent, B1=3, N=8, M=4, V=512, T=0.0, k_max=1, ws_bytes=None, logits=0x1000,
@@ -156,12 +157,13 @@ def test_greedy_partials_validation(lib):
     assert lib.sfv_lm_head_greedy_bytes(148, 512, 128, None) == sfv.SFV_E_INVAL
     nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 512, 128)[1]
     g = lib.sfv_lm_head_greedy
-    assert g(f, f, 32, 200, f, 128, 512, f, f, nb, None) == sfv.SFV_E_UNSUPPORTED
-    assert g(None, f, 148, 200, f, 128, 512, f, f, nb, None) == sfv.SFV_E_INVAL
-    assert g(f, f, 148, 200, f, 128, 512, f, None, nb, None) == sfv.SFV_E_INVAL
-    assert g(f, f, 148, 0, f, 128, 512, f, f, nb, None) == sfv.SFV_E_INVAL
-    assert g(f, f, 148, 200, f, 128, 512, f, P(0x1008), nb, None) == sfv.SFV_E_INVAL
-    assert g(f, f, 148, 200, f, 128, 512, f, f, nb - 16, None) == sfv.SFV_E_WORKSPACE
+    assert g(f, f, 32, 200, f, 128, 512, f, f, nb, None, None) == sfv.SFV_E_UNSUPPORTED
+    assert g(None, f, 148, 200, f, 128, 512, f, f, nb, None, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 200, f, 128, 512, f, None, nb, None, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 0, f, 128, 512, f, f, nb, None, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 200, f, 128, 512, f, P(0x1008), nb, None, None) == sfv.SFV_E_INVAL
+    assert g(f, f, 148, 200, f, 128, 512, f, f, nb - 16, None, None) == sfv.SFV_E_WORKSPACE
+    assert g(f, f, 148, 200, f, 128, 512, f, f, nb, P(0x1001), None) == sfv.SFV_E_INVAL  # misaligned status
 
 
 def test_step_attention_placement():
@@ -386,3 +388,12 @@ def test_commit_noalloc_limits(lib):
     big = [-1] + [0] * 63
     assert call(big, B1=64, N=256, M=64 * 256, V=151936) == sfv.SFV_E_WORKSPACE
     assert b"static" in lib.sfv_last_error()
+
+
+def test_gumbel_words_validation(lib):
+    """The word range may not run past 2^32; out must be non-null and aligned."""
+    P = ctypes.c_void_p
+    U = ctypes.c_uint32
+    assert lib.sfv_gumbel_words(U(2**32 - 4), U(5), P(0x1000), None) == sfv.SFV_E_INVAL
+    assert lib.sfv_gumbel_words(U(0), U(8), None, None) == sfv.SFV_E_INVAL
+    assert lib.sfv_gumbel_words(U(0), U(8), P(0x1002), None) == sfv.SFV_E_INVAL

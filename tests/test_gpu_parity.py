@@ -538,6 +538,47 @@ def test_lm_head_ragged(gpu_lib, M, D, V):
     assert err <= LOGIT_ABS
 
 
+@pytest.mark.parametrize("M", [20, 100, 300])
+def test_lm_head_row_status(gpu_lib, M):
+    """The optional status word of sfv_lm_head / sfv_lm_head_greedy: SFV_OK
+    for row ids in [0, R), SFV_E_INVAL when one is outside; the product still
+    reads only inside hidden (out-of-range ids read the nearest row) and the
+    in-range rows' logits are unchanged."""
+    rng = np.random.default_rng(40 + M)
+    D, V = 128, 1000
+    R = M + 5
+    hidden = synth.f32_to_bf16_bits(rng.standard_normal((R, D), dtype=np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal((V, D)) * 0.05).astype(np.float32))
+    rows = np.sort(rng.choice(R, M, replace=False)).astype(np.int32)
+    hd = torch.from_numpy(hidden).view(torch.bfloat16).cuda()
+    wd = torch.from_numpy(w).view(torch.bfloat16).cuda()
+    ref = O.lm_head(f32(hidden), rows, f32(w))
+    for bad in (None, R, -1, 1 << 30):
+        r = rows.copy()
+        if bad is not None:
+            r[M // 2] = bad
+        say(f"lm_head row status M={M} bad id={bad}")
+        rd = torch.from_numpy(r).cuda()
+        out = torch.full((M, V), float("nan"), dtype=torch.float32, device="cuda")
+        st = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+        gpu_lib.sfv_lm_head(hd, rd, M, R, wd, D, V, out, status=st)
+        calls = [("lm_head", out, st)]
+        if M > 32:
+            pb = gpu_lib.sfv_lm_head_greedy_bytes(M, V, D)
+            parts = torch.empty(pb, dtype=torch.uint8, device="cuda")
+            out2 = torch.full((M, V), float("nan"), dtype=torch.float32, device="cuda")
+            st2 = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+            gpu_lib.sfv_lm_head_greedy(hd, rd, M, R, wd, D, V, out2, parts, pb, status=st2)
+            calls.append(("lm_head_greedy", out2, st2))
+        torch.cuda.synchronize()
+        for name, o, s_ in calls:
+            assert int(s_.item()) == (O.SFV_OK if bad is None else -1), name
+            got = o.cpu().numpy()
+            assert np.all(np.isfinite(got))
+            keep = np.arange(M) != M // 2 if bad is not None else np.ones(M, bool)
+            assert np.max(np.abs(got[keep] - ref[keep])) <= LOGIT_ABS, name
+
+
 @pytest.mark.parametrize("fill", ["none", "all", "random"])
 def test_masked_rows_edges(gpu_lib, fill):
     rng = np.random.default_rng(2)
