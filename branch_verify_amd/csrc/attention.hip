@@ -174,30 +174,44 @@ __device__ __forceinline__ void tile_load(TileRegs<D>& tr, const Params& p, cons
     }
     return;
   }
-  const unsigned short* kbase;
-  const unsigned short* vbase;
-  size_t stride;
+  // The context rows are D elements apart (a compile-time stride, so the
+  // per-tile addresses are a uniform base plus shifts); block rows Hkv * D.
   if (r.ctx) {
-    kbase = p.k_ctx + ((size_t)g * p.L + r.key0) * D;
-    vbase = p.v_ctx + ((size_t)g * p.L + r.key0) * D;
-    stride = D;
-  } else {
-    kbase = p.k_blk + (((size_t)i_lo * p.N + r.key0) * p.Hkv + g) * D;
-    vbase = p.v_blk + (((size_t)i_lo * p.N + r.key0) * p.Hkv + g) * D;
-    stride = (size_t)p.Hkv * D;
+    const size_t tile0 = ((size_t)g * p.L + r.key0) * D;  // uniform
+    const unsigned short* kbase = p.k_ctx + tile0;
+    const unsigned short* vbase = p.v_ctx + tile0;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int c = t + kThreads * i;
+      const int key = min(c / parts, last);
+      tr.k[i] = ld16(kbase + key * D + (c % parts) * 8);
+    }
+    if (t < 2 * D) {
+      const int kg = t % 16, dg = t / 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int key = min(kg * 4 + q, last);
+        tr.v[q] = ld16(vbase + key * D + dg * 8);
+      }
+    }
+    return;
   }
+  const int stride = p.Hkv * D;
+  const size_t tile0 = (((size_t)i_lo * p.N + r.key0) * p.Hkv + g) * D;
+  const unsigned short* kbase = p.k_blk + tile0;
+  const unsigned short* vbase = p.v_blk + tile0;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     const int c = t + kThreads * i;
     const int key = min(c / parts, last);
-    tr.k[i] = ld16(kbase + key * stride + (c % parts) * 8);
+    tr.k[i] = ld16(kbase + (size_t)key * stride + (c % parts) * 8);
   }
   if (t < 2 * D) {
     const int kg = t % 16, dg = t / 16;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int key = min(kg * 4 + q, last);
-      tr.v[q] = ld16(vbase + key * stride + dg * 8);
+      tr.v[q] = ld16(vbase + (size_t)key * stride + dg * 8);
     }
   }
 }
