@@ -42,6 +42,7 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kRows = 128;     // query rows per workgroup, 32 per wave
 constexpr int kKeys = 64;      // keys per LDS tile
 constexpr int kPad = 8;        // bf16 elements of row padding of the key tiles in LDS
+constexpr int kSlots = 512;    // workgroups resident at once: two per CU, 256 CUs
 // Row padding of the transposed value tiles: a row is 34 dwords, so the
 // 8-byte reads of 32 consecutive rows (one per lane) fall on 32 distinct bank
 // pairs; with 36 dwords they met in pairs (two-way bank conflicts).
@@ -69,6 +70,8 @@ struct Params {
   const int32_t* rec_pos;  // folded path: index of each recomputed slot in qrows [B1][N]
   int B1, N, L, Hq, Hkv, G;
   int rows_total, row_tiles, splits, chunk;
+  int tile0, tiles;       // this launch's row tiles: tile0 .. tile0 + tiles - 1
+  int ws_row0, ws_rows;   // split states cover rows ws_row0 .. ws_row0 + ws_rows - 1
   float scale_log2;  // softmax scale * log2(e), applied inside the exp2
   bool causal;       // block keys visible only up to the row's own position
 };
@@ -248,8 +251,8 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int total = gridDim.x;
   const int lid = xcd_logical_block(blockIdx.x, total);
-  const int tile = lid % p.row_tiles;
-  const int gs = lid / p.row_tiles;
+  const int tile = p.tile0 + lid % p.tiles;
+  const int gs = lid / p.tiles;
   const int nsplit = MODE == kBlock ? 1 : p.splits;  // the block pass has no context splits
   const int split = gs % nsplit;
   const int g = gs / nsplit;
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
     }
     if (half == 0) p.lse[orow] = m_run * p.scale_log2 * 0.69314718055994531f + logf(l_tot);
   } else {
-    const size_t prow = ((size_t)split * p.Hkv + g) * p.rows_total + rho;
+    const size_t prow = ((size_t)split * p.Hkv + g) * p.ws_rows + (rho - p.ws_row0);
     float* op = p.ws + prow * D;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
     if (half == 0) {
-      const size_t nstate = (size_t)p.splits * p.Hkv * p.rows_total;
+      const size_t nstate = (size_t)p.splits * p.Hkv * p.ws_rows;
       float* mp = p.ws + nstate * D;
       mp[prow] = m_run * p.scale_log2;  // log2 domain (m_run is finite: every split sees a key)
       mp[nstate + prow] = l_tot;
@@ -493,26 +496,28 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
-// Log-sum-exp merge of the split states: one thread per (kv head, row, 4 dims).
+// Log-sum-exp merge of the split states of rows ws_row0 .. ws_row0 + ws_rows
+// - 1 (those below rows_total): one thread per (kv head, row, 4 dims).
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(Params p) {
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   constexpr int Q4 = D / 4;
-  const size_t n_items = (size_t)p.Hkv * p.rows_total * Q4;
+  const size_t n_items = (size_t)p.Hkv * p.ws_rows * Q4;
   if (tid >= n_items) return;
   const int q4 = tid % Q4;
-  const size_t gr = tid / Q4;  // g * rows_total + rho
-  const int g = gr / p.rows_total;
-  const int rho = gr % p.rows_total;
-  const size_t nstate = (size_t)p.splits * p.Hkv * p.rows_total;
+  const size_t gr = tid / Q4;  // g * ws_rows + (rho - ws_row0)
+  const int g = gr / p.ws_rows;
+  const int rho = p.ws_row0 + (int)(gr % p.ws_rows);
+  if (rho >= p.rows_total) return;
+  const size_t nstate = (size_t)p.splits * p.Hkv * p.ws_rows;
   const float* mp = p.ws + nstate * D;
   const float* lp = mp + nstate;
   float m = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, mp[(size_t)s * p.Hkv * p.rows_total + gr]);
+  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, mp[(size_t)s * p.Hkv * p.ws_rows + gr]);
   float z = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < p.splits; ++s) {
-    const size_t prow = (size_t)s * p.Hkv * p.rows_total + gr;
+    const size_t prow = (size_t)s * p.Hkv * p.ws_rows + gr;
     const float w = lp[prow] * exp2f(mp[prow] - m);
     const float4 v = *(const float4*)(p.ws + prow * D + q4 * 4);
     z += w;
@@ -531,15 +536,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(Params p) {
   if (q4 == 0) p.lse[orow] = m * 0.69314718055994531f + logf(z);
 }
 
+// One dense launch over the row tiles [p.tile0, p.tile0 + p.tiles) with
+// p.splits context splits, then (split) the merge of their states.
 template <int D>
-hipError_t launch_d(const Params& p, hipStream_t stream) {
-  const int blocks = p.row_tiles * p.Hkv * p.splits;
+hipError_t launch_dense_range(const Params& p, hipStream_t stream) {
+  const int blocks = p.tiles * p.Hkv * p.splits;
+  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((attn_kernel<D, kDense>), dim3(blocks), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const size_t items = (size_t)p.Hkv * p.rows_total * (D / 4);
+  const size_t items = (size_t)p.Hkv * p.ws_rows * (D / 4);
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// Dense attention: every row tile with the plan's splits; or, with a tail,
+// the row tiles before it unsplit and the tail's split over the context.
+template <int D>
+hipError_t launch_d(const Params& p0, const AttnPlan& plan, hipStream_t stream) {
+  Params p = p0;
+  p.tile0 = 0;
+  p.tiles = plan.row_tiles - plan.tail_tiles;
+  p.ws_row0 = 0;
+  p.ws_rows = plan.rows_total;
+  hipError_t e = launch_dense_range<D>(p, stream);
+  if (e != hipSuccess || plan.tail_tiles == 0) return e;
+  p.tile0 = plan.row_tiles - plan.tail_tiles;
+  p.tiles = plan.tail_tiles;
+  p.splits = plan.tail_splits;
+  p.chunk = plan.tail_chunk;
+  p.ws_row0 = p.tile0 * kRows;
+  p.ws_rows = plan.tail_tiles * kRows;
+  return launch_dense_range<D>(p, stream);
 }
 
 // Folded: context states of the recomputed rows, then every row's block keys
@@ -581,6 +609,32 @@ AttnPlan attn_plan(int B1, int N, int L, int Hq, int Hkv, int d) {
   pl.chunk = chunk;
   pl.ws_bytes = splits > 1 ? (size_t)splits * Hkv * pl.rows_total * (d + 2) * sizeof(float) : 0;
   pl.ws_bytes_folded = L > 0 ? (size_t)splits * Hkv * pl.rows_total * (d + 2) * sizeof(float) : 0;
+  // Tail split.  Unsplit, the workgroups run in rounds of kSlots (two per CU
+  // on 256 CUs); when they overshoot whole rounds by at most a quarter round,
+  // that last round would run a few long workgroups on a few CUs.  The row
+  // tiles of that remainder (the last ones of every kv head) are then split
+  // over the context into about kSlots short workgroups instead, whose states
+  // are merged, and the others run unsplit in whole rounds.
+  pl.tail_tiles = 0;
+  pl.tail_splits = 1;
+  pl.tail_chunk = chunk;
+  const int wgs = pl.row_tiles * Hkv;
+  const int rem = wgs % kSlots;
+  if (splits == 1 && L >= 2 * kKeys && wgs > kSlots && rem > 0 && rem <= kSlots / 4) {
+    const int tt = (rem + Hkv - 1) / Hkv;
+    int ts = kSlots / (tt * Hkv);
+    const int most = L / (2 * kKeys);  // at least two context tiles per split
+    if (ts > most) ts = most;
+    if (ts > 16) ts = 16;
+    if (ts >= 2) {
+      int tc = (L + ts - 1) / ts;
+      tc = (tc + kKeys - 1) / kKeys * kKeys;
+      pl.tail_tiles = tt;
+      pl.tail_splits = (L + tc - 1) / tc;
+      pl.tail_chunk = tc;
+      pl.ws_bytes = (size_t)pl.tail_splits * Hkv * (tt * kRows) * (d + 2) * sizeof(float);
+    }
+  }
   return pl;
 }
 
@@ -614,12 +668,16 @@ hipError_t launch_attention(const void* q, const void* k_blk, const void* v_blk,
   p.row_tiles = plan.row_tiles;
   p.splits = plan.splits;
   p.chunk = plan.chunk;
+  p.tile0 = 0;
+  p.tiles = plan.row_tiles;
+  p.ws_row0 = 0;
+  p.ws_rows = plan.rows_total;
   p.scale_log2 = scale * 1.4426950408889634f;
   const bool fold = rec_rows != nullptr;
   switch (d) {
-    case 32: return fold ? launch_folded_d<32>(p, stream) : launch_d<32>(p, stream);
-    case 64: return fold ? launch_folded_d<64>(p, stream) : launch_d<64>(p, stream);
-    case 128: return fold ? launch_folded_d<128>(p, stream) : launch_d<128>(p, stream);
+    case 32: return fold ? launch_folded_d<32>(p, stream) : launch_d<32>(p, plan, stream);
+    case 64: return fold ? launch_folded_d<64>(p, stream) : launch_d<64>(p, plan, stream);
+    case 128: return fold ? launch_folded_d<128>(p, stream) : launch_d<128>(p, plan, stream);
     default: return hipErrorInvalidValue;
   }
 }

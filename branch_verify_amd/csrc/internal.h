@@ -12,6 +12,8 @@ struct AttnPlan {
   int row_tiles;   // ceil(rows_total / 128)
   int splits;      // context key ranges
   int chunk;       // context keys per range (multiple of 64)
+  int tail_tiles;  // dense path: the last row tiles of every kv head, split apart (0: none)
+  int tail_splits, tail_chunk;  // their context ranges
   size_t ws_bytes;
   size_t ws_bytes_folded;  // folded path: context states of every row slot
 };

@@ -64,15 +64,34 @@ def test_attend_workspace_validation(lib):
     (2, 5, 1500, 8, 2, 64, 2),        # 750 keys rounded up to 768 a split: 2, the last ragged
     (3, 9, 3000, 4, 4, 32, 5),        # 640 keys a split: 5
     (1, 1, 511, 1, 1, 32, 1),         # below 512 keys: never split
+    (64, 64, 300, 32, 8, 64, 1),      # exactly two rounds of 512: no tail
 ])
 def test_attend_split_plan(lib, B1, N, L, Hq, Hkv, d, splits):
     """The split planner, seen through the workspace size: at least 512 context
     keys per split, as many splits as bring the grid to 512 workgroups; one
-    split needs no workspace."""
+    split needs no workspace unless the unsplit grid overshoots whole rounds
+    of 512 workgroups by at most 128: then the last ceil(overshoot / Hkv) row
+    tiles of every kv head are split over the context (at least two 64-key
+    tiles a split, at most 16 splits, about 512 workgroups) and only their
+    states need room."""
     rc, nb = _ws(lib.sfv_attend_workspace_bytes, B1, N, L, Hq, Hkv, d)
     assert rc == sfv.SFV_OK
     rows = B1 * N * (Hq // Hkv)
-    assert nb == (0 if splits == 1 else splits * Hkv * rows * (d + 2) * 4)
+    if splits > 1:
+        assert nb == splits * Hkv * rows * (d + 2) * 4
+        return
+    wgs = -(-rows // 128) * Hkv
+    over = wgs % 512
+    if wgs > 512 and 0 < over <= 128 and L >= 128:
+        tail = -(-over // Hkv)
+        ts = min(512 // (tail * Hkv), L // 128, 16)
+        chunk = -(-(-(-L // ts)) // 64) * 64
+        ts = -(-L // chunk)
+        assert nb == ts * Hkv * tail * 128 * (d + 2) * 4, (nb, tail, ts)
+        if (B1, N, L) == (33, 64, 4096):
+            assert (tail, ts) == (4, 16)
+    else:
+        assert nb == 0
 
 
 def test_attend_rejects_before_launch(lib):

@@ -494,6 +494,9 @@ def test_match_largest_tree(gpu_lib, hops, dup):
     dict(B1=3, N=256, L=130, Hq=2, Hkv=1, d=32),
     dict(B1=2, N=5, L=1500, Hq=8, Hkv=2, d=64),   # 2 context splits, the last one ragged
     dict(B1=3, N=9, L=3000, Hq=4, Hkv=4, d=32),   # 5 context splits, the last one ragged
+    # unsplit row tiles in whole rounds, then a split tail of the remaining ones
+    dict(B1=33, N=64, L=256, Hq=64, Hkv=8, d=128),  # 1024 + 4 x 8 tiles, tail in 2 splits
+    dict(B1=61, N=40, L=700, Hq=32, Hkv=4, d=32),   # 600 + 25 x 4 tiles, ragged last tile and split
 ])
 def test_attention_ragged(gpu_lib, shape):
     rng = np.random.default_rng(9)
