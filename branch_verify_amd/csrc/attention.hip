@@ -47,6 +47,11 @@ constexpr int kSlots = 512;    // workgroups resident at once: two per CU, 256 C
 // 8-byte reads of 32 consecutive rows (one per lane) fall on 32 distinct bank
 // pairs; with 36 dwords they met in pairs (two-way bank conflicts).
 constexpr int kVPad = 4;
+// The pipelined context pass keeps the softmax reference max until a row's
+// scores exceed it by more than this (log2 units): P <= 2^8, exact in scale
+// for bf16 and fp32, and the 2 * D / 32 * 16 rescale multiplies run only on
+// such a jump, not on every tile where some row's max moved.
+constexpr float kLazyLog2 = 8.f;
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -243,6 +248,296 @@ __device__ __forceinline__ void tile_store(Smem<D>& sm, int buf, const TileRegs<
   }
 }
 
+// Software-pipelined pass over the full context tiles 0 .. nf - 1 (nf >= 2)
+// of a workgroup's key range.  Step j computes the scores of tile j + 1 on
+// the matrix cores while the softmax of tile j runs on the vector ALUs, then
+// tile j's P V^T.  K is staged two tiles ahead and V one, in the same two
+// LDS buffers as the generic loop: step j reads K buffer (j + 1) & 1 and V
+// buffer j & 1, and stores K of tile j + 2 into K buffer j & 1 and V of tile
+// j + 1 into V buffer (j + 1) & 1, each last read in step j - 1 (one barrier
+// per step).  The scores, products and sums are the generic loop's, in its
+// order; only the softmax reference max moves lazily (kLazyLog2).
+//
+// A full context tile is kKeys * D contiguous elements: thread t's K chunks
+// sit at byte t * 16 + 4096 * i of it and its V rows at a fixed offset, so
+// the loads are a uniform tile base plus fixed 32-bit lane offsets.
+template <int D>
+__device__ __forceinline__ void ctx_load_k(TileRegs<D>& tr, const unsigned short* tile, unsigned klane) {
+  const char* b = reinterpret_cast<const char*>(tile);
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) tr.k[i] = ld16(b + (size_t)(klane + 4096u * i));
+}
+
+template <int D>
+__device__ __forceinline__ void ctx_load_v(TileRegs<D>& tr, const unsigned short* tile, unsigned vlane) {
+  if (2 * D >= kThreads || threadIdx.x < 2 * D) {
+    const char* b = reinterpret_cast<const char*>(tile);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tr.v[q] = ld16(b + (size_t)(vlane + 2u * D * q));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(Smem<D>& sm, int buf, const TileRegs<D>& tr) {
+  const int t = threadIdx.x;
+  constexpr int parts = D / 8;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int c = t + kThreads * i;
+    st16(&sm.k[buf][c / parts][(c % parts) * 8], tr.k[i]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_v(Smem<D>& sm, int buf, const TileRegs<D>& tr) {
+  const int t = threadIdx.x;
+  if (2 * D >= kThreads || t < 2 * D) {
+    const int kg = t % 16, dg = t / 16;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e / 2;
+      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      uint2 out;
+      out.x = __builtin_amdgcn_perm(tr.v[1][w], tr.v[0][w], sel);
+      out.y = __builtin_amdgcn_perm(tr.v[3][w], tr.v[2][w], sel);
+      *(uint2*)(&sm.vt[buf][dg * 8 + e][kg * 4]) = out;
+    }
+  }
+}
+
+// S^T of one key tile: 2 blocks of 32 keys x 32 rows, each summed over the
+// head dim in order s = 0, 1, ...  With AHEAD > 0 the key fragment of MFMA i
+// is read before MFMA i - AHEAD is issued; the fences order only LDS reads
+// and MFMAs, so vector ALU work (the softmax of the previous tile) is still
+// scheduled in between.
+template <int D, int AHEAD = 0>
+__device__ __forceinline__ void tile_scores(floatx16 (&st)[2], const Smem<D>& sm, int buf,
+                                            const u32x4 (&qf)[D / 16], int col, int half) {
+  constexpr int n = 2 * (D / 16);  // MFMAs: (s, kb) for s < D / 16, kb < 2
+  auto kread = [&](int i) { return ld16(&sm.k[buf][(i % 2) * 32 + col][(i / 2) * 16 + half * 8]); };
+  st[0] = floatx16{};
+  st[1] = floatx16{};
+  if (AHEAD == 0) {
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+      st[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kread(i)), as_bf16x8(qf[i / 2]), st[i % 2], 0,
+                                                          0, 0);
+    return;
+  }
+  constexpr int kAluMayCross = 0x0002 | 0x0004 | 0x0400;  // VALU, SALU, transcendental
+  u32x4 kf[n];
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) kf[i] = kread(i);
+  __builtin_amdgcn_sched_barrier(kAluMayCross);
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    if (i + AHEAD < n) kf[i + AHEAD] = kread(i + AHEAD);
+    st[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[i]), as_bf16x8(qf[i / 2]), st[i % 2], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(kAluMayCross);
+  }
+}
+
+// O^T += V^T P^T over one key tile (A = V^T rows, B = P^T), in the order
+// (kb, t2, b).  With AHEAD > 0 the value fragment of MFMA i is read before
+// MFMA i - AHEAD is issued (scheduling fences keep that order, so several
+// LDS reads are in flight while the matrix cores run).
+template <int D, int AHEAD = 0>
+__device__ __forceinline__ void tile_pv(floatx16 (&acc)[D / 32], const Smem<D>& sm, int buf,
+                                        const unsigned (&pk)[2][2][4], int col, int half) {
+  constexpr int DB = D / 32;
+  constexpr int n = 4 * DB;  // MFMAs of the tile
+  auto vread = [&](int i) {
+    const int kb = i / (2 * DB), t2 = (i / DB) % 2, b = i % DB;
+    const int kbase = kb * 32 + 16 * t2 + 4 * half;
+    const uint2 lo = *(const uint2*)(&sm.vt[buf][b * 32 + col][kbase]);
+    const uint2 hi = *(const uint2*)(&sm.vt[buf][b * 32 + col][kbase + 8]);
+    u32x4 vf;
+    vf[0] = lo.x;
+    vf[1] = lo.y;
+    vf[2] = hi.x;
+    vf[3] = hi.y;
+    return vf;
+  };
+  auto mfma = [&](int i, const u32x4& vf) {
+    const int kb = i / (2 * DB), t2 = (i / DB) % 2, b = i % DB;
+    u32x4 pb;
+    pb[0] = pk[kb][t2][0];
+    pb[1] = pk[kb][t2][1];
+    pb[2] = pk[kb][t2][2];
+    pb[3] = pk[kb][t2][3];
+    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pb), acc[b], 0, 0, 0);
+  };
+  if (AHEAD == 0) {
+#pragma unroll
+    for (int i = 0; i < n; ++i) mfma(i, vread(i));
+    return;
+  }
+  u32x4 vf[n];
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) vf[i] = vread(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    if (i + AHEAD < n) vf[i + AHEAD] = vread(i + AHEAD);
+    mfma(i, vf[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One pipelined step (tile j, parity PAR = j & 1); NEXT: tile j + 1 exists.
+template <int D, bool NEXT, int PAR>
+__device__ __forceinline__ void ctx_step(Smem<D>& sm, const unsigned short* kbase, const unsigned short* vbase,
+                                         unsigned klane, unsigned vlane, int j, int nf, float scale_log2,
+                                         const u32x4 (&qf)[D / 16], floatx16 (&cur)[2], floatx16 (&nxt)[2],
+                                         floatx16 (&acc)[D / 32], float& m_run, float& l_run, int col,
+                                         int half) {
+  constexpr size_t tile_elems = (size_t)kKeys * D;
+  TileRegs<D> tr;
+  const bool k2 = j + 2 < nf;
+  if (k2) ctx_load_k<D>(tr, kbase + (size_t)(j + 2) * tile_elems, klane);
+  if (NEXT) ctx_load_v<D>(tr, vbase + (size_t)(j + 1) * tile_elems, vlane);
+
+  // Softmax of tile j (no key is masked in a full context tile), in pieces:
+  // the running max over 8 scores at a time, then the max of the two
+  // half-waves, then the exponentials a pair of scores at a time.  The order
+  // of every sum and max is that of the generic loop.
+  float tmax = -INFINITY;
+  float m_new = 0.f, alpha = 1.f, mc = 0.f;
+  bool moved = false;
+  float psum = 0.f;
+  unsigned pk[2][2][4];
+  auto max_piece = [&](int q) {
+#pragma unroll
+    for (int i = 8 * q; i < 8 * q + 8; ++i) tmax = fmaxf(tmax, cur[i / 16][i % 16]);
+  };
+  auto finish_max = [&]() {
+    // the other half-wave's max (lane ^ 32) by a lane swap, not through LDS:
+    // the swap returns the low half's value in [0] and the high half's in [1]
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(tmax, __uint_as_float(half ? sw[0] : sw[1]));
+    // Lazy rescaling: the exponentials stay relative to the reference max
+    // m_run until some row's tile max exceeds it by more than kLazyLog2 (in
+    // log2 units), so P <= 2^kLazyLog2 and O and l hold their rescale; the
+    // reference then moves to the new max.
+    const bool far = (tmax - m_run) * scale_log2 > kLazyLog2 || m_run == -INFINITY;
+    m_new = __any(far) ? fmaxf(m_run, tmax) : m_run;
+    moved = m_new > m_run;
+    alpha = moved ? exp2_fast((m_run - m_new) * scale_log2) : 1.f;
+    mc = m_new == -INFINITY ? 0.f : m_new * scale_log2;
+  };
+  auto exp_pair = [&](int pidx) {  // scores 2 * pidx, 2 * pidx + 1 of block kb
+    const int kb = pidx / 8, r = (pidx % 8) * 2;
+    floatx2 pp;
+    pp[0] = exp2_fast(fmaf(cur[kb][r], scale_log2, -mc));
+    pp[1] = exp2_fast(fmaf(cur[kb][r + 1], scale_log2, -mc));
+    psum += pp[0] + pp[1];
+    pk[kb][r / 8][(r % 8) / 2] = __builtin_bit_cast(unsigned, __builtin_convertvector(pp, bf16x2));
+  };
+  if (NEXT) {
+    // The scores of tile j + 1 (n MFMAs, key fragments read two ahead), with
+    // the softmax of tile j dealt over them: the max in the first two MFMA
+    // slots, the 16 exponential pairs over the others.  Fences keep each
+    // slot's work in its slot.
+    constexpr int n = 2 * (D / 16);
+    constexpr int AH = 2;
+    const int nb = PAR ^ 1;
+    auto kread = [&](int i) { return ld16(&sm.k[nb][(i % 2) * 32 + col][(i / 2) * 16 + half * 8]); };
+    nxt[0] = floatx16{};
+    nxt[1] = floatx16{};
+    u32x4 kf[n];
+#pragma unroll
+    for (int i = 0; i < AH; ++i) kf[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      if (i + AH < n) kf[i + AH] = kread(i + AH);
+      nxt[i % 2] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[i]), as_bf16x8(qf[i / 2]), nxt[i % 2], 0, 0, 0);
+      if (i == 0) {
+        max_piece(0);
+        max_piece(1);
+      } else if (i == 1) {
+        max_piece(2);
+        max_piece(3);
+        finish_max();
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (2 + q * (n - 2) / 16 == i) exp_pair(q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) max_piece(q);
+    finish_max();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) exp_pair(q);
+  }
+  // Pin P here, beside the scores of tile j + 1, rather than letting the
+  // compiler sink its exponentials past the rescale branch (an empty asm
+  // statement that only names the registers; it emits no instruction).
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+      asm volatile("" : "+v"(pk[kb][t2][0]), "+v"(pk[kb][t2][1]), "+v"(pk[kb][t2][2]), "+v"(pk[kb][t2][3]));
+  asm volatile("" : "+v"(psum));
+  // O and l are rescaled only when some lane's running max moved.
+  if (__any(moved)) {
+    l_run *= alpha;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+  }
+  m_run = m_new;
+  l_run += psum;
+  tile_pv<D, 4>(acc, sm, PAR, pk, col, half);
+  if (k2) store_k<D>(sm, PAR, tr);
+  if (NEXT) store_v<D>(sm, PAR ^ 1, tr);
+  __syncthreads();
+}
+
+template <int D>
+__device__ __forceinline__ void ctx_pipelined(Smem<D>& sm, const Params& p, int g, int key0, int nf,
+                                              const u32x4 (&qf)[D / 16], floatx16 (&acc)[D / 32],
+                                              float& m_run, float& l_run, int col, int half) {
+  const int t = threadIdx.x;
+  const size_t base = ((size_t)g * p.L + key0) * D;
+  const unsigned short* kbase = p.k_ctx + base;
+  const unsigned short* vbase = p.v_ctx + base;
+  const unsigned klane = 16u * t;
+  const unsigned vlane = 2u * ((4u * (t % 16)) * D + 8u * (t / 16));
+  constexpr size_t tile_elems = (size_t)kKeys * D;
+  {
+    TileRegs<D> tr;
+    ctx_load_k<D>(tr, kbase, klane);
+    ctx_load_v<D>(tr, vbase, vlane);
+    store_k<D>(sm, 0, tr);
+    store_v<D>(sm, 0, tr);
+    ctx_load_k<D>(tr, kbase + tile_elems, klane);
+    store_k<D>(sm, 1, tr);
+  }
+  __syncthreads();
+  floatx16 sa[2], sb[2];
+  tile_scores<D>(sa, sm, 0, qf, col, half);
+  int j = 0;
+  for (; j + 2 < nf; j += 2) {
+    ctx_step<D, true, 0>(sm, kbase, vbase, klane, vlane, j, nf, p.scale_log2, qf, sa, sb, acc, m_run, l_run, col, half);
+    ctx_step<D, true, 1>(sm, kbase, vbase, klane, vlane, j + 1, nf, p.scale_log2, qf, sb, sa, acc, m_run, l_run, col,
+                         half);
+  }
+  if (j + 1 < nf) {
+    ctx_step<D, true, 0>(sm, kbase, vbase, klane, vlane, j, nf, p.scale_log2, qf, sa, sb, acc, m_run, l_run, col, half);
+    ctx_step<D, false, 1>(sm, kbase, vbase, klane, vlane, j + 1, nf, p.scale_log2, qf, sb, sa, acc, m_run, l_run, col,
+                          half);
+  } else {
+    ctx_step<D, false, 0>(sm, kbase, vbase, klane, vlane, j, nf, p.scale_log2, qf, sa, sb, acc, m_run, l_run, col,
+                          half);
+  }
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(Params p) {
   __shared__ Smem<D> sm;
@@ -297,14 +592,21 @@ __global__ __launch_bounds__(kThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 
                        : (MODE == kBlock || split == p.splits - 1) ? (i_hi - i_lo + 1) * p.N : 0;
   const int ntiles = ctx_tiles + (blk_keys + kKeys - 1) / kKeys;
 
+  // full context tiles: the pipelined pass; then the rest (a partial context
+  // tile, the block keys) in the generic loop
+  int j0 = 0;
+  if (MODE != kBlock && ctx_keys / kKeys >= 2) {
+    j0 = ctx_keys / kKeys;
+    ctx_pipelined<D>(sm, p, g, ctx_lo, j0, qf, acc, m_run, l_run, col, half);
+  }
   TileRegs<D> tr;
-  if (ntiles > 0) {
-    tile_load<D, MODE == kBlock>(tr, p, tile_range(p, 0, split, ctx_tiles, blk_keys), g, i_lo);
+  if (ntiles > j0) {
+    tile_load<D, MODE == kBlock>(tr, p, tile_range(p, j0, split, ctx_tiles, blk_keys), g, i_lo);
     tile_store<D>(sm, 0, tr);
   }
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+  for (int j = j0; j < ntiles; ++j) {
+    const int buf = (j - j0) & 1;
     const TileRange cur = tile_range(p, j, split, ctx_tiles, blk_keys);
     const bool more = j + 1 < ntiles;
     if (more) tile_load<D, MODE == kBlock>(tr, p, tile_range(p, j + 1, split, ctx_tiles, blk_keys), g, i_lo);
