@@ -545,14 +545,35 @@ hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
 // 256-row tiles alone compute 512).
 constexpr int kBigV = 256, kBigRows = 256;  // LDS rows of the large-tile kernel
 
+// The k-loop has an explicit instruction schedule: every MFMA sits in a
+// fenced slot (sched_barrier) that also carries a fixed share of the other
+// work.  The compiler, left to itself, read each A fragment into the same
+// registers right before its MFMAs and waited on it there.  Here:
+//  * A fragment q (k16 step q / NA, block q % NA) is read kSchedLA MFMA
+//    groups (of NB MFMAs) before its group, into a ring of kSchedLA + 1;
+//  * the next k16 step's B fragments are read kSchedGB groups before the
+//    step's last group;
+//  * the global loads of k-tile ks + 2 are spread over the first k16 step
+//    (their register set was stored to LDS in the previous k-tile), and the
+//    LDS stores of k-tile ks + 1 over steps kSchedSK .. end (their buffer was
+//    last read before the previous barrier).
+// The sums run in the same order as without the schedule: the logits are the
+// same bit for bit.
+constexpr int kSchedLA = 3;
+constexpr int kSchedGB = 1;
+constexpr int kSchedSK = 1;
+
 template <int WV, int NA, int NB>
 __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsigned short (*ws)[kBigV][LDK],
                                          unsigned short (*hs)[kBigRows][LDK]) {
   constexpr int NT = 512;
   constexpr int WM = 8 / WV;
   constexpr int TVB = WV * NA * 32, BR = WM * NB * 32;
-  constexpr int CA = TVB * 8 / NT;        // chunks of W per thread per k-tile
-  constexpr int CB = BR * 8 / NT;         // of hidden
+  constexpr int CA = TVB * 8 / NT;
+  constexpr int CB = BR * 8 / NT;
+  constexpr int NLD = CA + CB;      // global loads (and LDS stores) per thread per k-tile
+  constexpr int KK = BK / 16;       // k16 steps per k-tile
+  constexpr int SL = NA * NB;       // MFMA slots per k16 step
   static_assert(TVB * 8 % NT == 0 && BR * 8 % NT == 0, "tile rows must spread evenly over the threads");
   static_assert(TVB <= kBigV && BR <= kBigRows, "tile larger than its LDS");
   const int t = threadIdx.x;
@@ -560,8 +581,8 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
   const int wave = t / kWave;
   const int half = lane / 32;
   const int col = lane % 32;
-  const int wv = wave / WM;  // vocab group
-  const int wm = wave % WM;  // row group
+  const int wv = wave / WM;
+  const int wm = wave % WM;
 
   const unsigned short* wsrc[CA];
   const unsigned short* hsrc[CB];
@@ -575,28 +596,23 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
   for (int i = 0; i < CB; ++i) {
     const int c = t + NT * i;
     const int m = min(m0 + c / 8, p.M - 1);
-    const int hr = min(max(p.rows[m], 0), p.R - 1);  // never leave hidden
+    const int hr = min(max(p.rows[m], 0), p.R - 1);
     hsrc[i] = p.hidden + (size_t)hr * p.D + (c % 8) * 8;
   }
-  // two register sets: k-tile ks + 2 is loaded while ks + 1 waits in the
-  // other set for its turn in LDS
   u32x4 wreg[2][CA], hreg[2][CB];
-  auto fetch = [&](int k0, int set) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) wreg[set][i] = ld16(wsrc[i] + k0);
-#pragma unroll
-    for (int i = 0; i < CB; ++i) hreg[set][i] = ld16(hsrc[i] + k0);
+  auto load1 = [&](int k0, int set, int i) {  // global load i of a k-tile
+    if (i < CA)
+      wreg[set][i] = ld16(wsrc[i] + k0);
+    else
+      hreg[set][i - CA] = ld16(hsrc[i - CA] + k0);
   };
-  auto stash = [&](int buf, int set) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
+  auto store1 = [&](int buf, int set, int i) {  // LDS store i of a k-tile
+    if (i < CA) {
       const int c = t + NT * i;
       st16(&ws[buf][c / 8][(c % 8) * 8], wreg[set][i]);
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = t + NT * i;
-      st16(&hs[buf][c / 8][(c % 8) * 8], hreg[set][i]);
+    } else {
+      const int c = t + NT * (i - CA);
+      st16(&hs[buf][c / 8][(c % 8) * 8], hreg[set][i - CA]);
     }
   };
   floatx16 acc[NA][NB];
@@ -607,39 +623,66 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
 
   const int ksteps = p.D / BK;
   const int klast = (ksteps - 1) * BK;
-  fetch(0, 0);
-  fetch(min(BK, klast), 1);
-  stash(0, 0);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) load1(0, 0, i);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) load1(min(BK, klast), 1, i);
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) store1(0, 0, i);
   __syncthreads();
-  // k-tile ks is in LDS buffer ks & 1; its successor in register set
-  // (ks + 1) & 1; ks + 2 is loaded into set ks & 1 (past the end: re-reads of
-  // the last tile, L2 hits).  The loop is unrolled by four so that buffer and
-  // set indices are compile-time constants.
   for (int ks0 = 0; ks0 < ksteps; ks0 += 4) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int ks = ks0 + jj;
       if (ks >= ksteps) break;
       const int buf = jj & 1;
-      fetch(min((ks + 2) * BK, klast), buf);
+      const int knext2 = min((ks + 2) * BK, klast);
+      auto rdA = [&](int kk, int a) { return ld16(&ws[buf][wv * NA * 32 + a * 32 + col][kk * 16 + half * 8]); };
+      auto rdB = [&](int kk, int b) { return ld16(&hs[buf][wm * NB * 32 + b * 32 + col][kk * 16 + half * 8]); };
+      // A fragment q = kk * NA + a is read LA MFMA groups before its group,
+      // into ring entry q % (LA + 1); the B fragments of step kk one group
+      // before the step.
+      constexpr int LA = kSchedLA;
+      u32x4 fa[LA + 1], fb[2][NB];
+      auto readA = [&](int q) { fa[q % (LA + 1)] = rdA(q / NA, q % NA); };
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        u32x4 fa[NA], fb[NB];
+      for (int b = 0; b < NB; ++b) fb[0][b] = rdB(0, b);
 #pragma unroll
-        for (int a = 0; a < NA; ++a) fa[a] = ld16(&ws[buf][wv * NA * 32 + a * 32 + col][kk * 16 + half * 8]);
+      for (int q = 0; q < LA; ++q) readA(q);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) fb[b] = ld16(&hs[buf][wm * NB * 32 + b * 32 + col][kk * 16 + half * 8]);
+      for (int kk = 0; kk < KK; ++kk) {
+        const int bs = kk & 1;
 #pragma unroll
-        for (int a = 0; a < NA; ++a)
+        for (int a = 0; a < NA; ++a) {
+          const int q = kk * NA + a;
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[a]), as_bf16x8(fb[b]), acc[a][b], 0, 0, 0);
+          for (int b = 0; b < NB; ++b) {
+            const int slot = a * NB + b;  // within this k16 step
+            if (b == 0 && q + LA < KK * NA) readA(q + LA);
+            if (kk + 1 < KK && a == (NA > kSchedGB ? NA - 1 - kSchedGB : 0)) fb[bs ^ 1][b] = rdB(kk + 1, b);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[q % (LA + 1)]), as_bf16x8(fb[bs][b]),
+                                                                acc[a][b], 0, 0, 0);
+            // k-tile ks + 2's global loads over the first step, k-tile ks + 1's
+            // LDS stores over the others
+            if (kk == 0) {
+#pragma unroll
+              for (int i = 0; i < NLD; ++i)
+                if (i * SL / NLD == slot) load1(knext2, buf, i);
+            }
+            if (kk >= kSchedSK) {
+              const int s = (kk - kSchedSK) * SL + slot;  // 0 .. (KK - SK) * SL - 1
+#pragma unroll
+              for (int i = 0; i < NLD; ++i)
+                if (i * (KK - kSchedSK) * SL / NLD == s) store1(buf ^ 1, buf ^ 1, i);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
-      stash(buf ^ 1, buf ^ 1);
       __syncthreads();
     }
   }
-
   if (p.gpart) {
     // Greedy partial of every row over this 256-id vocab tile: a wave merges
     // its NA strips in id order, then the WV vocab groups are merged in id
