@@ -497,6 +497,7 @@ def test_match_largest_tree(gpu_lib, hops, dup):
     # unsplit row tiles in whole rounds, then a split tail of the remaining ones
     dict(B1=33, N=64, L=256, Hq=64, Hkv=8, d=128),  # 1024 + 4 x 8 tiles, tail in 2 splits
     dict(B1=61, N=40, L=700, Hq=32, Hkv=4, d=32),   # 600 + 25 x 4 tiles, ragged last tile and split
+    dict(B1=4, N=16, L=192, Hq=8, Hkv=2, d=64),     # three full context tiles, no partial one
 ])
 def test_attention_ragged(gpu_lib, shape):
     rng = np.random.default_rng(9)
