@@ -48,9 +48,10 @@ constexpr int kSlots = 512;    // workgroups resident at once: two per CU, 256 C
 // pairs; with 36 dwords they met in pairs (two-way bank conflicts).
 constexpr int kVPad = 4;
 // The pipelined context pass keeps the softmax reference max until a row's
-// scores exceed it by more than this (log2 units): P <= 2^8, exact in scale
-// for bf16 and fp32, and the 2 * D / 32 * 16 rescale multiplies run only on
-// such a jump, not on every tile where some row's max moved.
+// scores exceed it by more than this (log2 units): P <= 2^8, well inside the
+// range of bf16 and fp32, and the D / 2 rescale multiplies per lane (D / 32
+// accumulator blocks of 16) run only on such a jump, not on every tile where
+// some row's max moved.
 constexpr float kLazyLog2 = 8.f;
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
