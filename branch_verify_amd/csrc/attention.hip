@@ -494,7 +494,7 @@ __device__ __forceinline__ void ctx_step(Smem<D>& sm, const unsigned short* kbas
   }
   m_run = m_new;
   l_run += psum;
-  tile_pv<D, 4>(acc, sm, PAR, pk, col, half);
+  tile_pv<D, 3>(acc, sm, PAR, pk, col, half);
   if (k2) store_k<D>(sm, PAR, tr);
   if (NEXT) store_v<D>(sm, PAR ^ 1, tr);
   __syncthreads();
