@@ -706,26 +706,51 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
     }
   }
 
-  // lane holds vocab v0 + wv*128 + a*32 + 8*(r/4) + 4*half + r%4 of row m0 + wm*64 + b*32 + col
+  // Lane (col, half) holds vocab v0 + wv*NA*32 + a*32 + 8*(r/4) + 4*half + r%4
+  // of row m0 + wm*NB*32 + b*32 + col: stored straight from the registers, a
+  // store instruction would write 32 rows x 32 bytes.  Instead each wave
+  // stages a 32-row block of its tile in its own slice of the k-loop's LDS
+  // (rows of NA * 32 floats plus 4 of padding) and reads it back so that
+  // consecutive lanes hold consecutive ids of one row: every store
+  // instruction then writes whole 128-byte lines.
+  {
+    if (p.gpart) __syncthreads();  // the partials' LDS has been read
+    constexpr int TW = NA * 32;       // ids per wave row
+    constexpr int SROW = TW + 4;      // staged row stride (floats)
+    constexpr int C4 = TW / 4;        // float4 per row
+    static_assert(4 * 32 * SROW * 4 <= (int)sizeof(unsigned short) * 2 * kBigV * LDK, "LDS for staging");
+    // (the thread index passes through an empty asm statement here, so that
+    // nothing derived from it is computed before the k-loop, where every
+    // register is taken)
+    int tt = t;
+    asm volatile("" : "+v"(tt));
+    const int lane = tt % kWave, wave = tt / kWave, half = lane / 32, col = lane % 32;
+    // waves 0-3 stage in the weight buffers, 4-7 in the hidden ones
+    float* st = reinterpret_cast<float*>(wave < 4 ? &ws[0][0][0] : &hs[0][0][0]) + (wave % 4) * 32 * SROW;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int m = m0 + wm * NB * 32 + b * 32 + col;
-    if (m >= p.M) continue;
-    float* out = p.logits + (size_t)m * p.V;
+    for (int b = 0; b < NB; ++b) {
 #pragma unroll
-    for (int a = 0; a < NA; ++a) {
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int v = v0 + wv * NA * 32 + a * 32 + 8 * q4 + 4 * half;
-        const float4 val = make_float4(acc[a][b][4 * q4], acc[a][b][4 * q4 + 1], acc[a][b][4 * q4 + 2],
-                                       acc[a][b][4 * q4 + 3]);
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(floatx4*)&st[col * SROW + a * 32 + 8 * q4 + 4 * half] =
+              floatx4{acc[a][b][4 * q4], acc[a][b][4 * q4 + 1], acc[a][b][4 * q4 + 2], acc[a][b][4 * q4 + 3]};
+#pragma unroll
+      for (int i = 0; i < 32 * C4 / kWave; ++i) {
+        const int c = lane + kWave * i;
+        const int row = c / C4, f = (c % C4) * 4;
+        const floatx4 val = *(const floatx4*)&st[row * SROW + f];
+        const int m = m0 + wm * NB * 32 + b * 32 + row;
+        const int v = v0 + wv * NA * 32 + f;
+        if (m >= p.M) continue;
+        float* out = p.logits + (size_t)m * p.V;
         if (v + 3 < p.V && (p.V % 4) == 0) {
-          *(float4*)(out + v) = val;
+          *(floatx4*)(out + v) = val;
         } else {
-          if (v + 0 < p.V) out[v + 0] = val.x;
-          if (v + 1 < p.V) out[v + 1] = val.y;
-          if (v + 2 < p.V) out[v + 2] = val.z;
-          if (v + 3 < p.V) out[v + 3] = val.w;
+          if (v + 0 < p.V) out[v + 0] = val[0];
+          if (v + 1 < p.V) out[v + 1] = val[1];
+          if (v + 2 < p.V) out[v + 2] = val[2];
+          if (v + 3 < p.V) out[v + 3] = val[3];
         }
       }
     }
