@@ -555,13 +555,16 @@ constexpr int kBigV = 256, kBigRows = 256;  // LDS rows of the large-tile kernel
 //    step's last group;
 //  * the global loads of k-tile ks + 2 are spread over the first k16 step
 //    (their register set was stored to LDS in the previous k-tile), and the
-//    LDS stores of k-tile ks + 1 over steps kSchedSK .. end (their buffer was
-//    last read before the previous barrier).
+//    LDS stores of k-tile ks + 1 over the slots from step kSchedSK to the
+//    k-tile's barrier (their buffer was last read before the previous one);
+//  * the one barrier per k-tile comes kSchedTB groups before its end, so that
+//    the next k-tile's first fragments are read while its last MFMAs run.
 // The sums run in the same order as without the schedule: the logits are the
 // same bit for bit.
 constexpr int kSchedLA = 3;
 constexpr int kSchedGB = 1;
 constexpr int kSchedSK = 1;
+constexpr int kSchedTB = 2;
 
 template <int WV, int NA, int NB>
 __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsigned short (*ws)[kBigV][LDK],
@@ -630,6 +633,30 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
 #pragma unroll
   for (int i = 0; i < NLD; ++i) store1(0, 0, i);
   __syncthreads();
+  // A fragment q (k16 step q / NA, block q % NA) is read LA MFMA groups before
+  // its group, into ring entry q % (LA + 1); the B fragments of step kk + 1
+  // during step kk.  The ring runs on across k-tiles: the k-tile's one barrier
+  // comes TB groups before its end, once its own fragments are all read and
+  // the next k-tile's LDS stores are done, and the next k-tile's first
+  // fragments are read during those last TB groups.
+  constexpr int LA = kSchedLA;
+  constexpr int NG = KK * NA;            // MFMA groups (of NB) per k-tile
+  constexpr int TB = kSchedTB;           // groups after the barrier
+  constexpr int GBAR = NG - 1 - TB;      // the barrier follows this group
+  constexpr int GB = NA > kSchedGB ? NA - 1 - kSchedGB : 0;  // B read at this block of a step
+  static_assert(NG % (LA + 1) == 0 && KK % 2 == 0, "the fragment ring must wrap at k-tile ends");
+  static_assert(LA >= TB && LA + 1 <= NG, "own fragments read before the barrier");
+  static_assert((KK - 1) * NA + GB > GBAR && (KK - 2) * NA + GB <= GBAR, "B fragments on their side of the barrier");
+  constexpr int SW = (GBAR - kSchedSK * NA + 1) * NB;  // store slots, step kSchedSK .. the barrier
+  static_assert(SW >= NLD, "a slot for every LDS store");
+  u32x4 fa[LA + 1], fb[2][NB];
+  auto rdA = [&](int buf, int kk, int a) { return ld16(&ws[buf][wv * NA * 32 + a * 32 + col][kk * 16 + half * 8]); };
+  auto rdB = [&](int buf, int kk, int b) { return ld16(&hs[buf][wm * NB * 32 + b * 32 + col][kk * 16 + half * 8]); };
+#pragma unroll
+  for (int b = 0; b < NB; ++b) fb[0][b] = rdB(0, 0, b);
+#pragma unroll
+  for (int q = 0; q < LA; ++q) fa[q] = rdA(0, q / NA, q % NA);
+  __builtin_amdgcn_sched_barrier(0);
   for (int ks0 = 0; ks0 < ksteps; ks0 += 4) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -637,52 +664,49 @@ __device__ __forceinline__ void big_tile(const Params& p, int v0, int m0, unsign
       if (ks >= ksteps) break;
       const int buf = jj & 1;
       const int knext2 = min((ks + 2) * BK, klast);
-      auto rdA = [&](int kk, int a) { return ld16(&ws[buf][wv * NA * 32 + a * 32 + col][kk * 16 + half * 8]); };
-      auto rdB = [&](int kk, int b) { return ld16(&hs[buf][wm * NB * 32 + b * 32 + col][kk * 16 + half * 8]); };
-      // A fragment q = kk * NA + a is read LA MFMA groups before its group,
-      // into ring entry q % (LA + 1); the B fragments of step kk one group
-      // before the step.
-      constexpr int LA = kSchedLA;
-      u32x4 fa[LA + 1], fb[2][NB];
-      auto readA = [&](int q) { fa[q % (LA + 1)] = rdA(q / NA, q % NA); };
-#pragma unroll
-      for (int b = 0; b < NB; ++b) fb[0][b] = rdB(0, b);
-#pragma unroll
-      for (int q = 0; q < LA; ++q) readA(q);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int bs = kk & 1;
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
-          const int q = kk * NA + a;
+          const int g = kk * NA + a;
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const int slot = a * NB + b;  // within this k16 step
-            if (b == 0 && q + LA < KK * NA) readA(q + LA);
-            if (kk + 1 < KK && a == (NA > kSchedGB ? NA - 1 - kSchedGB : 0)) fb[bs ^ 1][b] = rdB(kk + 1, b);
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[q % (LA + 1)]), as_bf16x8(fb[bs][b]),
+            if (b == 0) {
+              // this k-tile's fragment g + LA, or the next k-tile's first ones
+              if (g + LA < NG) fa[(g + LA) % (LA + 1)] = rdA(buf, (g + LA) / NA, (g + LA) % NA);
+#pragma unroll
+              for (int q = 0; q < LA; ++q)
+                if (g == (GBAR + 1 > NG - LA + q ? GBAR + 1 : NG - LA + q)) fa[q] = rdA(buf ^ 1, q / NA, q % NA);
+            }
+            if (a == GB) fb[bs ^ 1][b] = kk + 1 < KK ? rdB(buf, kk + 1, b) : rdB(buf ^ 1, 0, b);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[g % (LA + 1)]), as_bf16x8(fb[bs][b]),
                                                                 acc[a][b], 0, 0, 0);
             // k-tile ks + 2's global loads over the first step, k-tile ks + 1's
-            // LDS stores over the others
+            // LDS stores over the slots from step kSchedSK to the barrier
             if (kk == 0) {
 #pragma unroll
               for (int i = 0; i < NLD; ++i)
                 if (i * SL / NLD == slot) load1(knext2, buf, i);
             }
-            if (kk >= kSchedSK) {
-              const int s = (kk - kSchedSK) * SL + slot;  // 0 .. (KK - SK) * SL - 1
+            if (g >= kSchedSK * NA && g <= GBAR) {
+              const int s = (g - kSchedSK * NA) * NB + b;
 #pragma unroll
               for (int i = 0; i < NLD; ++i)
-                if (i * (KK - kSchedSK) * SL / NLD == s) store1(buf ^ 1, buf ^ 1, i);
+                if (i * SW / NLD == s) store1(buf ^ 1, buf ^ 1, i);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (g == GBAR && b == NB - 1) {
+              __syncthreads();
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
-      __syncthreads();
     }
   }
+  __syncthreads();  // the last k-tile's reads of the (unused) next buffer are done
   if (p.gpart) {
     // Greedy partial of every row over this 256-id vocab tile: a wave merges
     // its NA strips in id order, then the WV vocab groups are merged in id
