@@ -12,11 +12,13 @@
 // Exactness: tokens and committed positions must equal the CPU definition
 // bit for bit.  The vocabulary sweep runs a fast fp32 path with a proven
 // error bound and re-decides exactly whatever falls inside the bound:
-//  * Gumbel keys: each lane evaluates g with hardware log2 (error below
-//    kGumbelEps, certified over all 2^32 words by sfv_selfcheck_bounds); the
-//    running best key of the wave is shared every 8 ids and any id whose fast
-//    key comes within the margin of it is re-evaluated with fp64 logarithms,
-//    exactly as defined.  The exact argmax is always among those.
+//  * Gumbel keys: each id's noise word falls in one of kGumbelBuckets runs
+//    of words, with fp32 bounds lo <= g <= hi on its exact value (a table,
+//    certified over all 2^32 words by sfv_selfcheck_bounds).  Rounding is
+//    monotone, so fl32(x + lo) <= key <= fl32(x + hi).  The wave keeps the
+//    best lower bound so far, and any id whose upper bound reaches it is
+//    re-evaluated with fp64 logarithms, exactly as defined.  The exact argmax
+//    is always among those.
 //  * S = sum exp(l - max l): fp32 exp2 terms summed in fp64, with a running
 //    bound E on |S - S_exact|.  A branch whose best and runner-up intervals
 //    [S - E, S + E] overlap is re-decided from S summed with fp64 exp.
@@ -24,6 +26,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "gumbel_bounds.h"
 #include "internal.h"
 #include "noise.h"
 
@@ -37,8 +40,6 @@ constexpr float kLog2e = kLog2eF;
 // error model of one fast term (internal.h): |t / exp(x - m) - 1| <= kC1 * a + kC2
 constexpr float kC1 = kExpC1;
 constexpr float kC2 = kExpC2;
-// Bound on |g_fast - g_exact| (certified below 1e-5 by the self-check).
-constexpr float kGumbelEps = 1.0f / 4096.0f;
 
 struct Item {
   int nrows;
@@ -85,21 +86,15 @@ size_t ws_bytes(int B1, int N, int M, int items_max, int splits) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// g = -ln(-ln u), u = (w + 1/2) 2^-32, in fp32 with hardware log2.  Branch
-// free (the lanes of a wave take different cases): -ln u is log2 of u, or of
-// 1 - e with e = 1 - u for the upper half, or for e < 1/128 the series of
-// -ln(1 - e) to e^4; the same values as evaluating only the case that holds.
-__device__ __forceinline__ float gumbel_fast(unsigned w) {
-  const float ln2 = 0.693147180559945309f;
-  const bool upper = w >= 0x80000000u;
-  const float u = ((float)w + 0.5f) * 2.3283064365386963e-10f;
-  const float e = ((float)(~w) + 0.5f) * 2.3283064365386963e-10f;  // 1 - u, in (0, 1/2] when upper
-  const float ser = e * (1.f + e * (0.5f + e * (0.33333333f + e * 0.25f)));
-  const float lg = -fast_log2(upper ? 1.f - e : u) * ln2;
-  const float L1 = (upper && e < 0.0078125f) ? ser : lg;  // -ln u > 0
-  return -fast_log2(L1) * ln2;
+// The bucket of a noise word in kGumbelBounds: w itself in the lower half
+// (u < 1/2), ~w in the upper half, classed by the sign, exponent and top 4
+// mantissa bits of its fp32 value (the generator's bucket_of_word).
+__device__ __forceinline__ int gumbel_bucket(unsigned w) {
+  const unsigned up = w >> 31;
+  const unsigned t = w ^ (0u - up);
+  const unsigned bits = __float_as_uint((float)t);
+  return (int)(max(bits, 0x3F780000u) >> 19) - 2031 + (int)(up * 498u);
 }
 
 // Lexicographic "better" for (value, index): larger value, then lower index.
@@ -264,11 +259,16 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
   __shared__ double red_d[kThreads / kWave][R];
   __shared__ float red_e[kThreads / kWave][R];
   __shared__ float wg_lmax[R];
+  __shared__ float2 gtab[NOISY ? kGumbelBuckets : 1];  // Gumbel bounds (lo, hi) per bucket
 
   const int item = blockIdx.x / a.splits;
   const int split = blockIdx.x % a.splits;
   if (NOISY && item >= *ws.count) return;  // at T = 0 there is one item per row, M in all
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  if (NOISY) {
+    for (int i = t; i < kGumbelBuckets; i += kThreads) gtab[i] = make_float2(kGumbelBounds[2 * i], kGumbelBounds[2 * i + 1]);
+    __syncthreads();
+  }
 
   int nrows, row[R];
   uint64_t step = 0, pos = 0;
@@ -356,10 +356,10 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
         xa[k][1] = *(const float4*)(rbase[k] + vc + 4);
       }
       unsigned wd[8];
-      float gf[8];
+      float2 gb[8];  // bounds on the Gumbel noise of the 8 ids
       noise_block(a.seed, step, pos, (uint64_t)(v >> 3), wd);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gf[e] = gumbel_fast(wd[e]);
+      for (int e = 0; e < 8; ++e) gb[e] = gtab[gumbel_bucket(wd[e])];
       // (predicated blocks, not breaks, so that every loop unrolls and the
       // small arrays stay in registers)
 #pragma unroll
@@ -371,23 +371,28 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
         if (k < nrows) {
           const float4 x0 = xa[k][0];
           const float4 x1 = xa[k][1];
-          // (an inactive lane's values are never used: the sums below are
-          // guarded and its Gumbel keys are -inf)
+          // (an inactive lane's values are never used: the sums below and
+          // the exact keys are guarded, and its key bounds are -inf)
           const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
           // running max / first argmax and the confidence sum (this lane's
           // ids), one max update per 8 ids as in the greedy sweep
           if (active) group8(x, v, lmax[k], lidx[k], S[k], E[k]);
-          float ka[8], lm = -INFINITY;
+          // key bounds fl32(x/T + lo) <= key <= fl32(x/T + hi); wbest is the
+          // wave's best lower bound so far, so every id whose key can reach
+          // the wave's largest key has its upper bound at or above it
+          float kh[8], lm = -INFINITY;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            ka[e] = active ? (UNIT_T ? x[e] : x[e] * a.inv_t) + gf[e] : -INFINITY;
-            lm = fmaxf(lm, ka[e]);
+            const float xs = UNIT_T ? x[e] : x[e] * a.inv_t;
+            kh[e] = active ? xs + gb[e].y : -INFINITY;
+            lm = fmaxf(lm, active ? xs + gb[e].x : -INFINITY);
           }
-          wbest[k] = fmaxf(wbest[k], wave_max_dpp(lm));
-          const float thr = wbest[k] - (2.f * kGumbelEps + 4.f * 1.1920929e-7f * fabsf(wbest[k]) + 1e-30f);
+          // (the wave max only when some lane's bound beats the best so far:
+          // otherwise it would leave wbest as it is)
+          if (__any(lm > wbest[k])) wbest[k] = fmaxf(wbest[k], wave_max_dpp(lm));
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            if (active && ka[e] >= thr) {
+            if (active && kh[e] >= wbest[k]) {
               const float key = (UNIT_T ? x[e] : x[e] * a.inv_t) + gumbel_exact(wd[e]);
               if (key > kmax[k]) {
                 kmax[k] = key;
@@ -854,13 +859,18 @@ __device__ __forceinline__ void atomic_max_pos_double(double* addr, double v) {
   atomicMax((unsigned long long*)addr, (unsigned long long)__double_as_longlong(v));
 }
 
+// out[0] = max over all 2^32 words of how far the exact noise value (the
+// exact path's gumbel_exact) lies outside its bucket's bounds: 0 certifies
+// the table.
 __global__ __launch_bounds__(256) void selfcheck_gumbel_kernel(double* out) {
   const uint64_t total = 1ull << 32;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   double worst = 0.0;
   for (uint64_t w = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; w < total; w += stride) {
-    const double err = fabs((double)gumbel_fast((unsigned)w) - gumbel_exact_f64((unsigned)w));
-    worst = fmax(worst, err);
+    const int b = gumbel_bucket((unsigned)w);
+    const double g = (double)gumbel_exact((unsigned)w);
+    const double lo = (double)kGumbelBounds[2 * b], hi = (double)kGumbelBounds[2 * b + 1];
+    worst = fmax(worst, fmax(lo - g, g - hi));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) worst = fmax(worst, __shfl_xor(worst, o, kWave));

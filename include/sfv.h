@@ -407,10 +407,12 @@ int sfv_match_tree(const int32_t* state, const int32_t* next_state, const int32_
                    int32_t* chain, int32_t* n_accepted, int32_t* status, void* stream);
 
 /*
- * Device self-check of the fast-path error bounds the commit relies on.
- * Sweeps every 32-bit noise word and every fp32 argument in [-126, 0] of the
- * fast exp2 and writes out[0] = max |g_fast - g_exact| over all words and
- * out[1] = max relative error of the fast exp2 (fp64 reference on the device).
+ * Device self-check of the fast-path bounds the commit relies on.  Sweeps
+ * every 32-bit noise word and every fp32 argument in [-126, 0] of the fast
+ * exp2 and writes out[0] = max over all words of how far the exact Gumbel
+ * value (fp64 logarithms, as the commit defines it) lies outside the bounds
+ * of its bucket in the sweep's table (0: every word inside), and out[1] = max
+ * relative error of the fast exp2 (fp64 reference on the device).
  *   out [2] fp64 device.  Synchronous on `stream`'s work only.
  */
 int sfv_selfcheck_bounds(double* out, void* stream);

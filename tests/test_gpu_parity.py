@@ -234,8 +234,8 @@ def test_selfcheck_bounds(gpu_lib):
     gpu_lib.sfv_selfcheck_bounds(out)
     torch.cuda.synchronize()
     g_err, e_rel = out.cpu().tolist()
-    say(f"max |g_fast - g| = {g_err:.3e}; max rel err exp2 = {e_rel:.3e}")
-    assert g_err < (1.0 / 4096) / 4          # commit margin uses 1/4096
+    say(f"max excess of g over its bucket's bounds = {g_err:.3e}; max rel err exp2 = {e_rel:.3e}")
+    assert g_err == 0.0                      # every word's exact noise inside its bucket
     assert e_rel < 2.0 ** -22                # commit error model uses 2^-20
 
 
