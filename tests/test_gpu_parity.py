@@ -384,6 +384,39 @@ def test_tie_breaks(gpu_lib):
     assert res["commit_pos"][0, 0] == 0 and res["token"][0] == 5
 
 
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_gumbel_key_near_ties(gpu_lib, T):
+    """Thousands of ids per row whose Gumbel keys fl32(fl32(l/T) + g) lie
+    within a few ulps of each other, many exactly equal: the sweep's screen
+    by per-bucket noise bounds must pass every one of them to the exact path,
+    and the token is the first argmax (lowest id on ties), as the oracle."""
+    V, N = 65536, 8
+    seed, step0, pos0 = 11, 70, 300
+    st = np.array([[-1, -1, 3, -1, -1, 5, -1, -1],
+                   [-1, 8, 3, -1, -1, 5, -1, -1],
+                   [-1, -1, 3, 2, -1, 5, -1, -1],
+                   [-1, 8, 3, -1, 6, 5, -1, -1]], np.int32)
+    parent = np.array([-1, 0, 0, 1], np.int32)
+    depth = O.tree_depths(parent)
+    rows = O.masked_rows(st)
+    rng = np.random.default_rng(17)
+    lg = (rng.standard_normal((rows.size, V)) * 1.3).astype(np.float32)
+    inv_t = np.float32(1.0) / np.float32(T)
+    for r, flat in enumerate(rows):
+        i, n = divmod(int(flat), N)
+        g = O.gumbel(seed, step0 + int(depth[i]), pos0 + n, np.arange(V)).astype(np.float64)
+        planted = rng.choice(V, 3000, replace=False)
+        # fl32(l / T) ~ 40 - g: keys within a few ulps of 40
+        lg[r, planted] = ((40.0 - g[planted]) * T).astype(np.float32)
+        keys = (lg[r] * inv_t).astype(np.float32) + O.gumbel(seed, step0 + int(depth[i]), pos0 + n, np.arange(V))
+        top = keys.max()
+        say(f"T={T} row {r}: {int(np.sum(keys == top))} ids at the max key, "
+            f"{int(np.sum(keys >= top - 4 * np.spacing(np.float32(40))))} within 4 ulps")
+    x = dict(state=st, parent=parent)
+    res = _run_commit_match(st, parent, V, T, seed, step0, pos0, lg)
+    check_commit_match(x, res, T, seed, step0, pos0, 1, logits_host=lg)
+
+
 def test_duplicate_draft_lowest_index(gpu_lib):
     V, N = 1024, 4
     st0 = np.array([-1, -1, 2, 3], np.int32)
