@@ -380,23 +380,31 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
           // key bounds fl32(x/T + lo) <= key <= fl32(x/T + hi); wbest is the
           // wave's best lower bound so far, so every id whose key can reach
           // the wave's largest key has its upper bound at or above it
-          float kh[8], lm = -INFINITY;
+          float kh[8], lm = -INFINITY, hm = -INFINITY;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float xs = UNIT_T ? x[e] : x[e] * a.inv_t;
-            kh[e] = active ? xs + gb[e].y : -INFINITY;
-            lm = fmaxf(lm, active ? xs + gb[e].x : -INFINITY);
+            kh[e] = xs + gb[e].y;
+            lm = fmaxf(lm, xs + gb[e].x);
+            hm = fmaxf(hm, kh[e]);
+          }
+          if (!active) {
+            lm = -INFINITY;
+            hm = -INFINITY;
           }
           // (the wave max only when some lane's bound beats the best so far:
           // otherwise it would leave wbest as it is)
           if (__any(lm > wbest[k])) wbest[k] = fmaxf(wbest[k], wave_max_dpp(lm));
+          // (the per-id tests only when some lane has a candidate)
+          if (__any(hm >= wbest[k])) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (active && kh[e] >= wbest[k]) {
-              const float key = (UNIT_T ? x[e] : x[e] * a.inv_t) + gumbel_exact(wd[e]);
-              if (key > kmax[k]) {
-                kmax[k] = key;
-                kidx[k] = v + e;
+            for (int e = 0; e < 8; ++e) {
+              if (active && kh[e] >= wbest[k]) {
+                const float key = (UNIT_T ? x[e] : x[e] * a.inv_t) + gumbel_exact(wd[e]);
+                if (key > kmax[k]) {
+                  kmax[k] = key;
+                  kidx[k] = v + e;
+                }
               }
             }
           }
