@@ -438,7 +438,7 @@ int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes) {
   const int ns = sfv::lm_head_greedy_parts(M, V, D);
   if (ns == 0) {
     return fail(SFV_E_UNSUPPORTED,
-                "greedy partials need M >= 33, D %% 64 == 0 and, for M <= 160, D >= 128 (M=%d, D=%d)", M, D);
+                "greedy partials need M >= 33 and D %% 64 == 0 (M=%d, D=%d)", M, D);
   }
   *bytes = (size_t)ns * M * sizeof(sfv::GreedyPart);
   return ok();

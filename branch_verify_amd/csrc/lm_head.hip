@@ -3,36 +3,22 @@
 //
 // SpecFold, Appendix B, keeps the LM head as a plain dense library product;
 // here it is the dominant step of a one-layer verify pass: the weight is
-// ~1.2 GB of bf16 and must be streamed from HBM once per pass.  All three
-// kernels compute the product transposed (vocab x rows), so that each lane
-// ends with 4 consecutive vocab ids of one row and stores them as one 16-byte
-// write of the row-major logits, and all gather the masked rows through `rows`.
+// ~1.2 GB of bf16 and must be streamed from HBM once per pass.  Both kernels
+// compute the product transposed (vocab x rows), so that each lane ends with
+// 4 consecutive vocab ids of one row, and both gather the masked rows through
+// `rows`.
 //
 // lm_head_tiled (M <= 32): 128 vocab x 128 rows x 64 k tiles, four waves of
 // 64 x 64, double-buffered LDS with the next k-tile prefetched into registers.
 //
-// lm_head_big8 (M > 160; MFMA-bound from a few hundred rows): 256-id vocab
-// tiles of 256 or 192 rows, eight waves, the next two k-tiles in flight; the
-// row tiles of one vocab tile get consecutive logical ids on one XCD, so the
-// weight tile they share is read from HBM once and then hit in L2.
-//
-// lm_head_stream (33..160 rows, the weight-streaming regime):
-//  * Every row of the padded row set is in one workgroup, so W is read from
-//    HBM exactly once and no MFMA work is spent on more than 31 pad rows.
-//  * Each wave owns 32 vocab rows and loads them from HBM straight into the
-//    MFMA A-operand registers, P k-stages ahead of use: no LDS round trip on
-//    the W path.  The reduction index k is permuted identically on both
-//    operands (slot (half, j) of step s holds k = 32*half + 8*s + j), which
-//    leaves the sum unchanged and makes a lane's 64 bytes per stage contiguous.
-//    Each quad of lanes loads whole 64-byte segments and a DPP quad transpose
-//    gives each lane its own (16-byte loads of one lane's segment, four rows
-//    per quad, reach the memory system as partial-line requests).
-//  * The gathered hidden rows (the operand the four waves share) are staged
-//    per 64-wide k-stage in double-buffered LDS.
-//  * Persistent workgroups (one or two per CU) walk their tiles over a
-//    flattened (tile, k-stage) index, so prefetch runs across tile boundaries
-//    and the 1187 vocab tiles (a prime count for V = 151936) spread within one
-//    tile.
+// lm_head_big8 (M > 32): 256-id vocab tiles of 256 or 192 rows, eight waves,
+// the next two k-tiles in flight; the row tiles of one vocab tile get
+// consecutive logical ids on one XCD, so the weight tile they share is read
+// from HBM once and then hit in L2.  From a few hundred rows on it is bound by
+// the MFMAs; below that by streaming the weight, which it does faster than a
+// kernel built for it (a weight-streaming kernel with every row in one
+// workgroup and W loaded straight into MFMA operand registers served 33..160
+// rows until this kernel overtook it at every row count).
 //
 // Every global load is unconditional: pad vocab ids and pad rows read a
 // clamped, in-bounds address and the outputs they pollute are never stored.
@@ -49,7 +35,6 @@ constexpr int BV = 128;  // vocab per tile
 constexpr int BM = 128;  // rows per tile
 constexpr int BK = 64;   // k per stage
 constexpr int LDK = BK + 8;
-constexpr int kStreamRows = 160;  // largest row count served by lm_head_stream
 constexpr int kTiledRows = 32;    // largest row count served by lm_head_tiled
 
 struct Params {
@@ -276,257 +261,6 @@ __device__ __forceinline__ void part_add(GreedyPart& r, const GreedyPart& e) {
   r.S = s;
   r.m = mx;
   r.idx = idx;
-}
-
-// Quad transpose of 16-byte elements: element i of quad lane p becomes element
-// p of quad lane i (two butterfly stages of DPP quad permutations).  The
-// weight is loaded with each group of four lanes reading 64 contiguous bytes
-// of one row; the transpose then hands every lane the MFMA operand it needs.
-template <int kCtrl>
-__device__ __forceinline__ unsigned dpp_quad(unsigned x) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, true);
-}
-
-__device__ __forceinline__ void quad_transpose4(u32x4 (&a)[4]) {
-  const int p = threadIdx.x & 3;
-  u32x4 c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = dpp_quad<0xB1>(a[i ^ 1][d]);  // quad_perm [1,0,3,2]
-    c[i] = (((i ^ p) & 1) == 0) ? a[i] : o;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = dpp_quad<0x4E>(c[i ^ 2][d]);  // quad_perm [2,3,0,1]
-    a[i] = (((i ^ p) & 2) == 0) ? c[i] : o;
-  }
-}
-
-template <int MB, int VW, int P, int OCC, int HS = 1, bool QUAD = (OCC == 2)>
-__global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void lm_head_stream(Params p) {
-  constexpr int MP = MB * 32;
-  // LDS rows allocated: with OCC = 1, at least 81 KB, so that one workgroup fills a CU
-  constexpr int MPA = (OCC == 1 && MP < 288) ? 288 : MP;
-  constexpr int SK = 64;
-  constexpr int LDH = SK + 8;
-  constexpr int TV = 128 * VW;  // vocab ids per tile
-  __shared__ unsigned short hs[2][MPA][LDH];
-  __shared__ GreedyPart gx[4 * VW][MP];  // greedy partials of a tile's strips (when p.gpart)
-
-  const int t = threadIdx.x;
-  const int lane = t % kWave;
-  const int wave = t / kWave;
-  const int r = lane % 32;
-  const int half = lane / 32;
-  const int ksteps = p.D / SK;
-  const int ntiles = (p.V + TV - 1) / TV;
-  const int my_tiles = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int total = my_tiles * ksteps;  // a multiple of P (the launcher checks ksteps % P)
-
-  // hidden chunk c = t + 256*i -> padded row c / 8, k part c % 8 (same for every tile)
-  const unsigned short* hsrc[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int c = t + kThreads * i;
-    const int m = min(c / (SK / 8), p.M - 1);
-    const int hr = min(max(p.rows[m], 0), p.R - 1);  // never leave hidden
-    hsrc[i] = p.hidden + (size_t)hr * p.D + (c % (SK / 8)) * 8;
-  }
-  // Lane (r, half) multiplies W row tile*TV + wave*32*VW + 32*b + r, k range
-  // [k0 + 32 half, +32) of each stage.  With QUAD, load s of quad q fetches
-  // that segment of quad lane s's (row, half), 16 bytes per lane of the quad,
-  // so each load instruction asks for 16 whole 64-byte segments instead of 64
-  // partial ones, and quad_transpose4 then puts every segment in its own lane
-  // (the one-workgroup-per-CU variants, with more rows, lack the registers
-  // for the transpose and load their own segments).
-  const int qsel = QUAD ? 4 * (lane / 4) : lane;
-  const int qpart = QUAD ? 8 * (lane % 4) : 0;
-
-  // W comes from HBM and is prefetched P stages ahead; hidden comes from L2
-  // and is loaded one stage ahead (registers are the limit on prefetch depth).
-  u32x4 wreg[P][VW][4];
-  u32x4 hreg[MB];
-  // Flattened stage g (clamped to the last one: a re-read, an L2 hit).
-  auto stage_tile = [&](int g) { return (int)blockIdx.x + (min(g, total - 1) / ksteps) * (int)gridDim.x; };
-  auto stage_k = [&](int g) { return (min(g, total - 1) % ksteps) * SK; };
-  auto load_w = [&](u32x4 (&wd)[VW][4], int g) {
-    const int tile = stage_tile(g);
-    const int k0 = stage_k(g);
-#pragma unroll
-    for (int b = 0; b < VW; ++b) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int pl = QUAD ? qsel + s : qsel;  // the lane whose segment this load fetches
-        const int v = min(tile * TV + wave * 32 * VW + 32 * b + pl % 32, p.V - 1);
-        wd[b][s] = ld16(p.w + (size_t)v * p.D + k0 + 32 * (pl / 32) + (QUAD ? qpart : 8 * s));
-      }
-    }
-  };
-  auto load_h = [&](int g) {
-    const int k0 = stage_k(g);
-#pragma unroll
-    for (int i = 0; i < MB; ++i) hreg[i] = ld16(hsrc[i] + k0);
-  };
-  auto store_h = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int c = t + kThreads * i;
-      st16(&hs[buf][c / (SK / 8)][(c % (SK / 8)) * 8], hreg[i]);
-    }
-  };
-
-  floatx16 acc[VW][MB];
-#pragma unroll
-  for (int b = 0; b < VW; ++b)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[b][mb] = floatx16{};
-
-  if (total > 0) {
-    load_h(0);
-#pragma unroll
-    for (int j = 0; j < P; ++j) load_w(wreg[j], j);
-    store_h(0);
-    __syncthreads();
-  }
-  for (int g0 = 0; g0 < total; g0 += P) {
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int g = g0 + j;
-      const int buf = g & 1;
-      load_h(g + 1);
-      if (QUAD) {
-#pragma unroll
-        for (int b = 0; b < VW; ++b) quad_transpose4(wreg[j][b]);
-      }
-      // The hidden fragments of a group of 4 / HS k-steps are all read before
-      // its first MFMA (the scheduling barrier keeps them together), so the
-      // group pays one LDS latency instead of one per fragment; HS > 1 trades
-      // that for registers.
-      constexpr int SPG = 4 / HS;
-#pragma unroll
-      for (int hg = 0; hg < HS; ++hg) {
-        u32x4 hf[SPG][MB];
-#pragma unroll
-        for (int s2 = 0; s2 < SPG; ++s2)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) hf[s2][mb] = ld16(&hs[buf][mb * 32 + r][32 * half + 8 * (hg * SPG + s2)]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s2 = 0; s2 < SPG; ++s2) {
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-            for (int b = 0; b < VW; ++b)
-              acc[b][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wreg[j][b][hg * SPG + s2]),
-                                                                   as_bf16x8(hf[s2][mb]), acc[b][mb], 0, 0, 0);
-          }
-        }
-      }
-      load_w(wreg[j], g + P);
-      store_h(buf ^ 1);
-      if (g % ksteps == ksteps - 1) {  // last stage of a tile: write it out
-        const int tile = (int)blockIdx.x + (g / ksteps) * (int)gridDim.x;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int m = mb * 32 + r;
-          if (m < p.M) {
-            float* out = p.logits + (size_t)m * p.V;
-#pragma unroll
-            for (int b = 0; b < VW; ++b) {
-              const int vb = tile * TV + wave * 32 * VW + 32 * b;
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) {
-                const int v = vb + 8 * q4 + 4 * half;
-                const float4 val = make_float4(acc[b][mb][4 * q4], acc[b][mb][4 * q4 + 1],
-                                               acc[b][mb][4 * q4 + 2], acc[b][mb][4 * q4 + 3]);
-                if (v + 3 < p.V && (p.V % 4) == 0) {
-                  *(float4*)(out + v) = val;
-                } else {
-                  if (v + 0 < p.V) out[v + 0] = val.x;
-                  if (v + 1 < p.V) out[v + 1] = val.y;
-                  if (v + 2 < p.V) out[v + 2] = val.z;
-                  if (v + 3 < p.V) out[v + 3] = val.w;
-                }
-              }
-            }
-          }
-          if (p.gpart) {  // (uniform) greedy partials of this row's 32-id strips, to LDS
-#pragma unroll
-            for (int b = 0; b < VW; ++b) {
-              const int strip = tile * 4 * VW + wave * VW + b;
-              const GreedyPart gp = strip_partial(acc[b][mb], strip * 32 + 4 * half, p.V);
-              if (half == 0) gx[wave * VW + b][m] = gp;
-            }
-          }
-#pragma unroll
-          for (int b = 0; b < VW; ++b) acc[b][mb] = floatx16{};
-        }
-      }
-      __syncthreads();
-      if (p.gpart && g % ksteps == ksteps - 1 && t < p.M) {
-        // the tile's partial of row t: its strips in id order (gx is next
-        // written a whole tile later, after as many barriers)
-        GreedyPart r = gx[0][t];
-#pragma unroll
-        for (int k = 1; k < 4 * VW; ++k) part_add(r, gx[k][t]);
-        const int tile = (int)blockIdx.x + (g / ksteps) * (int)gridDim.x;
-        p.gpart[(size_t)tile * p.M + t] = r;
-      }
-    }
-  }
-}
-
-int cu_count() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
-template <int MB, int VW, int P, int OCC = 1, int HS = 1>
-hipError_t launch_stream(const Params& p, hipStream_t stream) {
-  if ((p.D / 64) % P != 0) return hipErrorInvalidValue;
-  const int ntiles = (p.V + 128 * VW - 1) / (128 * VW);
-  const int grid = min(ntiles, OCC * cu_count());
-  hipLaunchKernelGGL((lm_head_stream<MB, VW, P, OCC, HS>), dim3(grid), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-// 33..160 rows: two workgroups share a CU (2-stage prefetch, registers for
-// two waves per SIMD).  Above 160 rows the large-tile kernel is faster (on the
-// SDAR-8B head: 397-401 against 418-421 us at 176-192 rows, 471-475 against
-// 530-796 us at 240-256): its 256-id vocab tiles re-read the hidden rows half
-// as often, and it needs no register-starved one-workgroup-per-CU variant.
-template <int MB>
-hipError_t launch_stream_two(const Params& p, hipStream_t stream) {
-  if ((p.D / 64) % 2 == 0) return launch_stream<MB, 1, 2, 2>(p, stream);
-  return launch_stream<MB, 1, 1, 2>(p, stream);
-}
-
-hipError_t launch_stream_rows(const Params& p, hipStream_t stream) {
-  const int ks = p.D / 64;
-  switch ((p.M + 31) / 32) {
-    case 2:
-      return launch_stream_two<2>(p, stream);
-    case 3:
-      return launch_stream_two<3>(p, stream);
-    case 4:
-      return launch_stream_two<4>(p, stream);
-    case 5:
-      if (ks % 2 == 0) return launch_stream<5, 1, 2, 2>(p, stream);
-      return launch_stream<5, 1, 1, 2>(p, stream);
-    default:
-      return hipErrorInvalidValue;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -862,25 +596,18 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
   p.mt = (M + BM - 1) / BM;
   p.gpart = nullptr;
   p.big_a = p.big_b = 0;
-  // Up to 32 rows: the tiled kernel.  33..160 rows: stream the weight once
-  // past every row (from 33 rows on it beats the tiled kernel, whose row
-  // tile re-reads the hidden rows with one k-tile in flight).  More rows: the
-  // large-tile kernel.
+  // Up to 32 rows: the tiled kernel.  More: the large-tile kernel (from 33
+  // rows on it beats the tiled kernel, whose row tile re-reads the hidden
+  // rows with one k-tile in flight).
   if (M <= kTiledRows) return launch_tiled(p, stream);
-  if (M <= kStreamRows) return launch_stream_rows(p, stream);
   return launch_big8(p, stream);
 }
 
-// From 33 rows on, the LM head writes one greedy partial per row and vocab
-// tile beside the logits: 128-id tiles in the weight-streaming kernel (up to
-// 160 rows), 256-id tiles in the large-tile kernel.
+// From 33 rows on, the LM head (the large-tile kernel) writes one greedy
+// partial per row and 256-id vocab tile beside the logits.
 int lm_head_greedy_parts(int M, int V, int D) {
   if (M <= kTiledRows || D % 64 != 0 || V < 1) return 0;
-  // weight-streaming kernel: 128-id tiles; two or more k-stages per tile (a
-  // barrier separates the reads of a tile's strip partials from the next
-  // tile's writes)
-  if (M <= kStreamRows) return D >= 128 ? (V + 127) / 128 : 0;
-  return (V + kBigV - 1) / kBigV;  // large-tile kernel: 256-id tiles
+  return (V + kBigV - 1) / kBigV;
 }
 
 hipError_t launch_lm_head_greedy(const void* hidden, const int32_t* rows, int M, int R, const void* w,
@@ -899,8 +626,7 @@ hipError_t launch_lm_head_greedy(const void* hidden, const int32_t* rows, int M,
   p.mt = (M + BM - 1) / BM;
   p.gpart = gpart;
   p.big_a = p.big_b = 0;
-  if (M > kStreamRows) return launch_big8(p, stream);
-  return launch_stream_rows(p, stream);
+  return launch_big8(p, stream);
 }
 
 }  // namespace sfv

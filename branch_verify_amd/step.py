@@ -55,8 +55,8 @@ class VerifyStep:
         self.logits = torch.empty((max(1, M), V), dtype=torch.float32, device=dev)
         self.commit_ws_bytes = sfv.sfv_commit_workspace_bytes(B1, N, M, V)
         self.commit_ws = torch.empty(max(1, self.commit_ws_bytes), dtype=torch.uint8, device=dev)
-        # greedy steps in the weight-streaming regime: the LM head writes tile
-        # partials and the commit reads those instead of the logits
+        # greedy steps from 33 rows on: the LM head writes tile partials and
+        # the commit reads those instead of the logits
         self.parts_bytes = sfv.sfv_lm_head_greedy_bytes(M, V, D) if (fuse and self.T == 0.0) else 0
         self.fuse = self.parts_bytes > 0
         if self.fuse:

@@ -272,9 +272,9 @@ int sfv_masked_rows(const int32_t* state, int B1, int N, int32_t* rows, int32_t*
  * outside hidden), so such a row's logits are another row's.  To detect them,
  * pass `status` (device int32, or NULL): before the product a one-workgroup
  * scan of rows writes *status = SFV_E_INVAL if any id is outside [0, R), else
- * SFV_OK.  Kernel by M: up to 32 rows a tiled kernel, 33..160 a weight-streaming kernel
- * (the weight read from HBM once past every row), above that 256-id vocab
- * tiles of 256 or 192 rows.
+ * SFV_OK.  Kernel by M: up to 32 rows a tiled kernel, above that 256-id vocab
+ * tiles of 256 or 192 rows (the row tiles of a vocab tile side by side, so
+ * the weight is read from HBM once).
  */
 int sfv_lm_head(const void* hidden, const int32_t* rows, int M, int R,
                 const void* w, int D, int V, float* logits, int32_t* status, void* stream);
@@ -356,7 +356,7 @@ int sfv_commit_noalloc(const float* logits, const int32_t* rows, int M,
  * argmax).
  *
  * sfv_lm_head_greedy: as sfv_lm_head (status included), and the kernel also reduces every
- * vocabulary tile of every row (128 ids up to 160 rows, 256 ids above) to its
+ * vocabulary tile of 256 ids of every row to its
  * max, the lowest id attaining it and a fast fp32 sum of exp(l - max) with a
  * bound on its error.
  *   partials: device buffer of sfv_lm_head_greedy_bytes(M, V, D) bytes,
@@ -368,8 +368,8 @@ int sfv_commit_noalloc(const float* logits, const int32_t* rows, int M,
  *   partials, D: as written by sfv_lm_head_greedy for the same M, V, D;
  *   logits, rows, state, parent_host, outputs: as for sfv_commit;
  *   workspace: sfv_commit_greedy_workspace_bytes(B1, N, M, V) bytes.
- * Supported: M >= 33, D % 64 == 0, and D >= 128 when M <= 160 (other shapes
- * return SFV_E_UNSUPPORTED), V % 8 == 0, V < 2^31 / 8, 1 <= k_max <= N, tau
+ * Supported: M >= 33 and D % 64 == 0 (other shapes return
+ * SFV_E_UNSUPPORTED), V % 8 == 0, V < 2^31 / 8, 1 <= k_max <= N, tau
  * finite when k_max > 1.
  */
 int sfv_lm_head_greedy_bytes(int M, int V, int D, size_t* bytes);

@@ -159,19 +159,18 @@ def test_commit_validation(lib):
 def test_greedy_partials_validation(lib):
     P = ctypes.c_void_p
     f = P(0x1000)
+    # from 33 rows on: one 16-byte partial per row and 256-id vocab tile
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 151936, 4096)
-    assert rc == sfv.SFV_OK and nb == (151936 + 127) // 128 * 148 * 16
+    assert rc == sfv.SFV_OK and nb == (151936 + 255) // 256 * 148 * 16
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 160, 1000, 128)
-    assert rc == sfv.SFV_OK and nb == 8 * 160 * 16
-    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 161, 1000, 64)  # above 160 rows: 256-id tiles
+    assert rc == sfv.SFV_OK and nb == 4 * 160 * 16
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 161, 1000, 64)
     assert rc == sfv.SFV_OK and nb == 4 * 161 * 16
-    for M, D in [(32, 128), (0, 128), (148, 100), (148, 64), (257, 100), (64, 64)]:
+    for M, D in [(32, 128), (0, 128), (148, 100), (257, 100), (1, 64)]:
         assert _ws(lib.sfv_lm_head_greedy_bytes, M, 512, D)[0] == sfv.SFV_E_UNSUPPORTED, (M, D)
-    # above 256 rows: one partial per 256-id tile, D = 64 allowed
-    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 257, 1000, 64)
-    assert rc == sfv.SFV_OK and nb == 4 * 257 * 16
-    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 33, 1000, 128)  # 33..128 rows: the streaming kernel too
-    assert rc == sfv.SFV_OK and nb == 8 * 33 * 16
+    for M in (33, 64, 148, 257):  # D = 64 at every supported row count
+        rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, M, 1000, 64)
+        assert rc == sfv.SFV_OK and nb == 4 * M * 16, M
     assert _ws(lib.sfv_lm_head_greedy_bytes, -1, 512, 128)[0] == sfv.SFV_E_INVAL
     assert lib.sfv_lm_head_greedy_bytes(148, 512, 128, None) == sfv.SFV_E_INVAL
     nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 512, 128)[1]
@@ -227,7 +226,6 @@ def test_commit_greedy_validation(lib):
     assert _commit_greedy(lib, par, M=32) == sfv.SFV_E_UNSUPPORTED    # the tiled kernel writes no partials
     assert _commit_greedy(lib, par, V=500) == sfv.SFV_E_UNSUPPORTED
     assert _commit_greedy(lib, par, D=100) == sfv.SFV_E_UNSUPPORTED
-    assert _commit_greedy(lib, par, D=64) == sfv.SFV_E_UNSUPPORTED
     assert _commit_greedy(lib, par, k_max=0) == sfv.SFV_E_INVAL
     assert _commit_greedy(lib, par, k_max=33) == sfv.SFV_E_INVAL
     assert _commit_greedy(lib, par, k_max=2, tau=float("nan")) == sfv.SFV_E_INVAL

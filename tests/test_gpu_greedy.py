@@ -5,9 +5,8 @@ T = 0), through the C ABI.
 The sweep path is pinned to the oracle bit for bit on seeded host logits
 (test_gpu_parity); here the partials path must give the same logits (the same
 kernel arithmetic), the same tokens, committed positions and next states, and
-confidences within the fast path's bound, on shapes served by both kernels
-that write partials (33..160 rows: the weight-streaming kernel, 128-id tiles;
-above: the large-tile kernel, 256-id tiles, mixed row-tile heights), ragged
+confidences within the fast path's bound, on shapes the large-tile kernel
+serves from 33 rows on (256-id tiles, one or both row-tile heights), ragged
 vocabularies whose last tile is partly past V, at the full SDAR-8B-like and
 D3D packed-tray shapes, with the threshold commit, and on planted exact and
 near ties that force the fp64 re-decision.  On every case the pair's outputs
