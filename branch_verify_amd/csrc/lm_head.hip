@@ -44,7 +44,7 @@ struct Params {
   float* logits;
   int M, D, V, R;
   int vt, mt;          // tile counts
-  GreedyPart* gpart;   // weight-streaming kernel only: tile partials [vocab tiles][M], or null
+  GreedyPart* gpart;   // large-tile kernel only: tile partials [vocab tiles][M], or null
   int big_a, big_b;    // large-tile kernel: row tiles of 256 rows, then of 192
 };
 
@@ -160,18 +160,9 @@ __global__ __launch_bounds__(kThreads) void lm_head_tiled(Params p) {
   }
 }
 
-
 // ---------------------------------------------------------------------------
-// persistent weight-streaming kernel: OCC workgroups per CU
+// greedy tile partials
 // ---------------------------------------------------------------------------
-// A workgroup tile is 128*VW vocab ids x all (padded) rows; the hidden rows
-// are the operand the whole tile shares and are re-read from L2 once per
-// tile.  Each of the OCC * (CU count) workgroups walks tiles blockIdx.x,
-// blockIdx.x + gridDim.x, ... over a flattened (tile, k-stage) index: W is
-// prefetched P stages ahead straight across tile boundaries, and the tiles
-// per workgroup differ by at most one.  With OCC = 1 the LDS is padded so that
-// no second workgroup fits a CU; with OCC = 2 two workgroups share each CU, so
-// one's LDS and barrier waits overlap the other's MFMAs.
 // Greedy partial of one row over a 32-id strip held by a lane pair: this
 // lane's 16 values are ids v0 + 8 q + j (q, j < 4; the partner lane, 32
 // away, holds v0 + 4 + 8 q + j).  Ids at or past V are left out.  Both lanes
