@@ -210,17 +210,23 @@ __global__ __launch_bounds__(kThreads) void commit_plan_kernel(const int32_t* ro
 // vocabulary sweep of one work item over one vocab range
 // ---------------------------------------------------------------------------
 // Adds 8 consecutive ids v .. v + 7 of one row to its running max, first
-// argmax and confidence sum: one max update per 8 ids, the 8 fast terms
-// summed in fp32 (at most 7 roundings of a sum of positive terms: below
-// 2^-21 of it) and the group sum added in fp64, with the bound E.
+// argmax (IDX only: the sampled commit takes its token from the keys, and
+// the maximum's value does not depend on it) and confidence sum: one max
+// update per 8 ids, the 8 fast terms summed in fp32 (at most 7 roundings of a
+// sum of positive terms: below 2^-21 of it) and the group sum added in fp64,
+// with the bound E.
+template <bool IDX>
 __device__ __forceinline__ void group8(const float (&x)[8], int v, float& lmax, int& lidx, double& S, float& E) {
   float m8 = x[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, x[e]);
   if (m8 > lmax) {
-    int e8 = 7;
+    if constexpr (IDX) {
+      int e8 = 7;
 #pragma unroll
-    for (int e = 6; e >= 0; --e) e8 = x[e] == m8 ? e : e8;
+      for (int e = 6; e >= 0; --e) e8 = x[e] == m8 ? e : e8;
+      lidx = v + e8;
+    }
     if (lmax != -INFINITY) {
       const float af = m8 - lmax;
       const float f = fast_exp2(-af * kLog2e);
@@ -228,11 +234,14 @@ __device__ __forceinline__ void group8(const float (&x)[8], int v, float& lmax, 
       E = E * f + (float)S * (kC1 * af + kC2);
     }
     lmax = m8;
-    lidx = v + e8;
   }
-  float gs = 0.f, ga = 0.f;  // sum of terms, sum of term * argument
+  // sum of terms and sum of term * argument, started from the first term
+  // (0 + t is t for every t >= 0, so the sums are those of a zero start)
+  const float am0 = lmax - x[0];
+  const float t0 = fast_exp2(-am0 * kLog2e);
+  float gs = t0, ga = t0 * am0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 1; e < 8; ++e) {
     const float am = lmax - x[e];
     const float tt = fast_exp2(-am * kLog2e);
     gs += tt;
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
     auto take8 = [&](const float4& x0, const float4& x1, int v) {
       if (v >= ve) return;  // ve and v are multiples of 8
       const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      group8(x, v, lmax[0], lidx[0], S[0], E[0]);
+      group8<true>(x, v, lmax[0], lidx[0], S[0], E[0]);
     };
     float4 a0, a1, b0, b1;
     load8(a0, a1, vb + 8 * t);
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
           const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
           // running max / first argmax and the confidence sum (this lane's
           // ids), one max update per 8 ids as in the greedy sweep
-          if (active) group8(x, v, lmax[k], lidx[k], S[k], E[k]);
+          if (active) group8<false>(x, v, lmax[k], lidx[k], S[k], E[k]);
           // key bounds fl32(x/T + lo) <= key <= fl32(x/T + hi); wbest is the
           // wave's best lower bound so far, so every id whose key can reach
           // the wave's largest key has its upper bound at or above it
