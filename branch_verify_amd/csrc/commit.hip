@@ -102,6 +102,13 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// The exact key fl32(fl32(l_v / T) + g) of id v of a row, g from its noise word.
+template <bool UNIT_T>
+__device__ __forceinline__ float exact_key_t(const float* row, int v, unsigned w, float inv_t) {
+  const float x = row[v];
+  return (UNIT_T ? x : x * inv_t) + gumbel_exact(w);
+}
+
 // ---------------------------------------------------------------------------
 // masked-row scan (one workgroup)
 // ---------------------------------------------------------------------------
@@ -261,8 +268,11 @@ struct RowsArgs {
 };
 
 // UNIT_T: T = 1, where l * (1/T) = l exactly and the multiply is left out.
+// Four waves per SIMD (at most 128 registers): the sampled sweep is bound by
+// VALU issue and loses more from a lower occupancy than it saves elsewhere.
 template <bool NOISY, int R, bool UNIT_T = false>
-__global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLayout ws) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void commit_rows_kernel(RowsArgs a,
+                                                                                                   WsLayout ws) {
   __shared__ float red_f[kThreads / kWave][R][2];
   __shared__ int red_i[kThreads / kWave][R][2];
   __shared__ double red_d[kThreads / kWave][R];
@@ -274,6 +284,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
   const int split = blockIdx.x % a.splits;
   if (NOISY && item >= *ws.count) return;  // at T = 0 there is one item per row, M in all
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   if (NOISY) {
     for (int i = t; i < kGumbelBuckets; i += kThreads) gtab[i] = make_float2(kGumbelBounds[2 * i], kGumbelBounds[2 * i + 1]);
     __syncthreads();
@@ -284,6 +295,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
   if (NOISY) {
     const Item it = ws.items[item];
     nrows = it.nrows;
+    __builtin_assume(nrows >= 1);  // the plan writes no empty item
 #pragma unroll
     for (int k = 0; k < R; ++k) row[k] = k < nrows ? it.rows[k] : -1;
     step = a.step0 + (uint64_t)it.level;
@@ -299,6 +311,10 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
   float lmax[R], E[R], wbest[R], kmax[R];
   int lidx[R], kidx[R];
   double S[R];
+  // T > 0: the lane's best key candidate so far as an interval blo <= key <=
+  // bhi (equal once its exact key is known), its id and noise word
+  float blo[R], bhi[R];
+  unsigned bwd[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     lmax[k] = -INFINITY;
@@ -308,6 +324,9 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
     wbest[k] = -INFINITY;
     kmax[k] = -INFINITY;
     kidx[k] = 0x7FFFFFFF;
+    blo[k] = -INFINITY;
+    bhi[k] = -INFINITY;
+    bwd[k] = 0;
   }
 
   // Logit loads are unconditional: a lane past the range end reads the last
@@ -405,20 +424,60 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
           // otherwise it would leave wbest as it is)
           if (__any(lm > wbest[k])) wbest[k] = fmaxf(wbest[k], wave_max_dpp(lm));
           // (the per-id tests only when some lane has a candidate)
+          // A candidate replaces the lane's best when its interval lies above
+          // the best's; where the two overlap, their exact keys decide (larger
+          // key, then lower id); one whose upper end does not pass the best's
+          // lower end cannot win (a tie at that end goes to the best, whose id
+          // is lower: a lane meets its ids in increasing order).
           if (__any(hm >= wbest[k])) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              if (active && kh[e] >= wbest[k]) {
-                const float key = (UNIT_T ? x[e] : x[e] * a.inv_t) + gumbel_exact(wd[e]);
-                if (key > kmax[k]) {
-                  kmax[k] = key;
+              if (active && kh[e] >= wbest[k] && kh[e] > blo[k]) {
+                const float xs = UNIT_T ? x[e] : x[e] * a.inv_t;
+                const float lo = xs + gb[e].x;
+                if (lo > bhi[k]) {
+                  blo[k] = lo;
+                  bhi[k] = kh[e];
                   kidx[k] = v + e;
+                  bwd[k] = wd[e];
+                } else {
+                  const float ke = xs + gumbel_exact(wd[e]);
+                  const float kb = blo[k] == bhi[k] ? blo[k] : exact_key_t<UNIT_T>(rbase[k], kidx[k], bwd[k], a.inv_t);
+                  if (better(ke, v + e, kb, kidx[k])) {
+                    kidx[k] = v + e;
+                    bwd[k] = wd[e];
+                    blo[k] = bhi[k] = ke;
+                  } else {
+                    blo[k] = bhi[k] = kb;
+                  }
                 }
               }
             }
           }
         }
       }
+    }
+  }
+
+  // The thread index after the sweep is rebuilt from the wave's index (a
+  // uniform value) and the lane id, so that no register holds it through the
+  // loop.
+  const int we = wave_u;
+  int le;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+  const int te = we * kWave + le;
+
+  if constexpr (NOISY) {
+    // Every id whose key can reach the wave's largest key has its upper end
+    // at or above wbest, and the lane's best is the only such id of the lane
+    // that can win: its exact key enters the reduction.
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (k >= nrows) break;
+      if (bhi[k] != -INFINITY && bhi[k] >= wbest[k])
+        kmax[k] = blo[k] == bhi[k] ? blo[k] : exact_key_t<UNIT_T>(rbase[k], kidx[k], bwd[k], a.inv_t);
+      else
+        kidx[k] = 0x7FFFFFFF;
     }
   }
 
@@ -447,23 +506,23 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
         }
       }
     }
-    if (lane == 0) {
-      red_f[wave][k][0] = bm;
-      red_i[wave][k][0] = bi;
-      red_f[wave][k][1] = km;
-      red_i[wave][k][1] = ki;
+    if (le == 0) {
+      red_f[we][k][0] = bm;
+      red_i[we][k][0] = bi;
+      red_f[we][k][1] = km;
+      red_i[we][k][1] = ki;
     }
   }
   __syncthreads();
-  if (t < R && t < nrows) {
-    float bm = red_f[0][t][0];
-    int bi = red_i[0][t][0];
+  if (te < R && te < nrows) {
+    float bm = red_f[0][te][0];
+    int bi = red_i[0][te][0];
     for (int w = 1; w < kThreads / kWave; ++w)
-      if (better(red_f[w][t][0], red_i[w][t][0], bm, bi)) {
-        bm = red_f[w][t][0];
-        bi = red_i[w][t][0];
+      if (better(red_f[w][te][0], red_i[w][te][0], bm, bi)) {
+        bm = red_f[w][te][0];
+        bi = red_i[w][te][0];
       }
-    wg_lmax[t] = bm;
+    wg_lmax[te] = bm;
   }
   __syncthreads();
 #pragma unroll
@@ -482,31 +541,31 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
       s += __shfl_xor(s, o, kWave);
       e += __shfl_xor(e, o, kWave);
     }
-    if (lane == 0) {
-      red_d[wave][k] = s;
-      red_e[wave][k] = e;
+    if (le == 0) {
+      red_d[we][k] = s;
+      red_e[we][k] = e;
     }
   }
   __syncthreads();
-  if (t < R && t < nrows) {
+  if (te < R && te < nrows) {
     double s = 0.0;
     float e = 0.f;
-    float km = red_f[0][t][1];
-    int ki = red_i[0][t][1];
+    float km = red_f[0][te][1];
+    int ki = red_i[0][te][1];
     for (int w = 0; w < kThreads / kWave; ++w) {
-      s += red_d[w][t];
-      e += red_e[w][t];
-      if (w && better(red_f[w][t][1], red_i[w][t][1], km, ki)) {
-        km = red_f[w][t][1];
-        ki = red_i[w][t][1];
+      s += red_d[w][te];
+      e += red_e[w][te];
+      if (w && better(red_f[w][te][1], red_i[w][te][1], km, ki)) {
+        km = red_f[w][te][1];
+        ki = red_i[w][te][1];
       }
     }
-    float bm = red_f[0][t][0];
-    int bi = red_i[0][t][0];
+    float bm = red_f[0][te][0];
+    int bi = red_i[0][te][0];
     for (int w = 1; w < kThreads / kWave; ++w)
-      if (better(red_f[w][t][0], red_i[w][t][0], bm, bi)) {
-        bm = red_f[w][t][0];
-        bi = red_i[w][t][0];
+      if (better(red_f[w][te][0], red_i[w][te][0], bm, bi)) {
+        bm = red_f[w][te][0];
+        bi = red_i[w][te][0];
       }
     Partial pr;
     pr.lmax = bm;
@@ -516,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void commit_rows_kernel(RowsArgs a, WsLay
     pr.S = s;
     pr.E = e * 1.0001f + (float)(s * 1e-13);
     pr.pad = 0;
-    ws.part[(size_t)row[t] * a.splits + split] = pr;
+    ws.part[(size_t)row[te] * a.splits + split] = pr;
   }
 }
 
