@@ -35,7 +35,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerIter = 8 * kThreads;  // vocab ids per workgroup iteration
-constexpr int kItemRows = kItemRowsHost;  // rows sharing one noise sweep
+constexpr int kItemRows = kItemRowsHost;
+// The widest Gumbel bucket with 1% to spare: the distance from an id's upper key
+// bound down to a certain lower bound of its key, beside the rounding term.
+constexpr float kLowSlack = kGumbelMaxWidth * 1.01f;  // rows sharing one noise sweep
 constexpr float kLog2e = kLog2eF;
 // error model of one fast term (internal.h): |t / exp(x - m) - 1| <= kC1 * a + kC2
 constexpr float kC1 = kExpC1;
@@ -405,21 +408,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           // running max / first argmax and the confidence sum (this lane's
           // ids), one max update per 8 ids as in the greedy sweep
           if (active) group8<false>(x, v, lmax[k], lidx[k], S[k], E[k]);
-          // key bounds fl32(x/T + lo) <= key <= fl32(x/T + hi); wbest is the
-          // wave's best lower bound so far, so every id whose key can reach
-          // the wave's largest key has its upper bound at or above it
-          float kh[8], lm = -INFINITY, hm = -INFINITY;
+          // key bounds fl32(x/T + lo) <= key <= fl32(x/T + hi); wbest is a
+          // lower bound of the wave's largest key so far, so every id whose key
+          // can reach that key has its upper bound at or above it
+          float kh[8], hm = -INFINITY;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float xs = UNIT_T ? x[e] : x[e] * a.inv_t;
             kh[e] = xs + gb[e].y;
-            lm = fmaxf(lm, xs + gb[e].x);
             hm = fmaxf(hm, kh[e]);
           }
-          if (!active) {
-            lm = -INFINITY;
-            hm = -INFINITY;
-          }
+          if (!active) hm = -INFINITY;
+          // A lower bound of the key of the id whose upper bound is hm: its lower
+          // bound lies at most the widest bucket below, plus the two fp32
+          // roundings (each below 2^-24 of the sum), both covered with margin.
+          const float lm = hm - fmaf(fabsf(hm), 0x1p-21f, kLowSlack);
           // (the wave max only when some lane's bound beats the best so far:
           // otherwise it would leave wbest as it is)
           if (__any(lm > wbest[k])) wbest[k] = fmaxf(wbest[k], wave_max_dpp(lm));

@@ -101,3 +101,43 @@ def test_a_wrong_table_is_caught(gen, table):
         gg = O.gumbel_from_words(ww)
         bad += int(((gg < lo2[r_b]) | (gg > hi2[r_b])).any())
     assert bad > 0
+
+
+def test_max_width_covers_every_bucket(gen, table):
+    lo, hi, _ = table
+    w = gen.max_width(lo, hi)
+    ok = np.isfinite(lo)
+    widths = hi[ok].astype(np.float64) - lo[ok].astype(np.float64)
+    assert float(w) >= widths.max()
+    assert float(np.nextafter(w, np.float32(0))) < widths.max()  # rounded up, not padded
+    with open(gen.HEADER) as f:
+        assert f"kGumbelMaxWidth = {gen._lit(w)};" in f.read()
+
+
+def _lower_from_upper(hm, width):
+    """The sweep's lower bound hm - fma(|hm|, 2^-21, 1.01 * width), one rounding
+    per fp32 operation (the fma's single rounding taken in fp64, where the
+    product and sum are exact)."""
+    slack = np.float32(np.float32(width) * np.float32(1.01))
+    d = (np.abs(hm).astype(np.float64) * 2.0 ** -21 + np.float64(slack)).astype(np.float32)
+    return (hm - d).astype(np.float32)
+
+
+def test_lower_bound_from_upper_bound(gen, table):
+    # An id's key fl32(x + g) is at least the sweep's lower bound derived from its
+    # upper bound fl32(x + hi): the widest bucket plus both fp32 roundings.
+    lo, hi, _ = table
+    width = gen.max_width(lo, hi)
+    rng = np.random.default_rng(20261204)
+    n = 1_000_000
+    w = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    scale = np.float32(10.0) ** rng.integers(-2, 7, n).astype(np.float32)
+    x = (rng.standard_normal(n).astype(np.float32) * scale).astype(np.float32)
+    b = gen.bucket_of_word(w)
+    key = (x + O.gumbel_from_words(w)).astype(np.float32)
+    up = (x + hi[b]).astype(np.float32)
+    assert (key <= up).all()
+    assert (_lower_from_upper(up, width) <= key).all()
+    # without the rounding term the bound fails at large |x|
+    slack = np.float32(np.float32(width) * np.float32(1.01))
+    assert ((up - slack).astype(np.float32) > key).any()
