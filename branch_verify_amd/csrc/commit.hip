@@ -261,6 +261,40 @@ __device__ __forceinline__ void group8(const float (&x)[8], int v, float& lmax, 
   E += kC1 * ga + (kC2 + 4.76837158e-7f) * gs;
 }
 
+// The sampled sweep's form of group8: S and E are kept against a reference ref
+// that moves only when a group's max passes it by more than kLazyMargin, so
+// they are rescaled at a lane's first group and rarely after (each term is at
+// most e^kLazyMargin, and the error model holds with |a|); the running max is
+// kept beside it for the confidence.  No index: the sampled commit takes its
+// token from the keys.
+__device__ __forceinline__ void group8_lazy(const float (&x)[8], float& lmax, float& ref, double& S, float& E) {
+  float m8 = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, x[e]);
+  lmax = fmaxf(lmax, m8);
+  if (m8 - ref > kLazyMargin) {  // (a difference, exact when the two are close: no rounding of ref + margin)
+    if (ref != -INFINITY) {
+      const float af = m8 - ref;
+      const float f = fast_exp2(-af * kLog2e);
+      S *= (double)f;
+      E = E * f + (float)S * (kC1 * af + kC2);
+    }
+    ref = m8;
+  }
+  const float am0 = ref - x[0];
+  const float t0 = fast_exp2(-am0 * kLog2e);
+  float gs = t0, ga = t0 * fabsf(am0);
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    const float am = ref - x[e];
+    const float tt = fast_exp2(-am * kLog2e);
+    gs += tt;
+    ga += tt * fabsf(am);
+  }
+  S += (double)gs;
+  E += kC1 * ga + (kC2 + 4.76837158e-7f) * gs;
+}
+
 struct RowsArgs {
   const float* logits;
   const int32_t* rows;
@@ -318,6 +352,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // bhi (equal once its exact key is known), its id and noise word
   float blo[R], bhi[R];
   unsigned bwd[R];
+  float sref[R];  // T > 0: the reference S and E are kept against (group8_lazy)
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     lmax[k] = -INFINITY;
@@ -330,6 +365,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     blo[k] = -INFINITY;
     bhi[k] = -INFINITY;
     bwd[k] = 0;
+    sref[k] = -INFINITY;
   }
 
   // Logit loads are unconditional: a lane past the range end reads the last
@@ -407,7 +443,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
           // running max / first argmax and the confidence sum (this lane's
           // ids), one max update per 8 ids as in the greedy sweep
-          if (active) group8<false>(x, v, lmax[k], lidx[k], S[k], E[k]);
+          if (active) group8_lazy(x, lmax[k], sref[k], S[k], E[k]);
           // key bounds fl32(x/T + lo) <= key <= fl32(x/T + hi); wbest is a
           // lower bound of the wave's largest key so far, so every id whose key
           // can reach that key has its upper bound at or above it
@@ -534,8 +570,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const float M = wg_lmax[k];
     double s = 0.0;
     float e = 0.f;
-    if (lmax[k] != -INFINITY) {
-      const double f = exp((double)lmax[k] - (double)M);  // fp64: exact to ~1 ulp
+    // (S and E are kept against lmax in the greedy sweep, against sref in the
+    // sampled one)
+    const float sr = NOISY ? sref[k] : lmax[k];
+    if (sr != -INFINITY) {
+      const double f = exp((double)sr - (double)M);  // fp64: exact to ~1 ulp
       s = S[k] * f;
       e = (float)((double)E[k] * f) + (float)s * 1e-12f;
     }
@@ -965,12 +1004,15 @@ __global__ __launch_bounds__(256) void gumbel_words_kernel(uint32_t first, uint3
 }
 
 __global__ __launch_bounds__(256) void selfcheck_exp2_kernel(double* out) {
-  // every fp32 x in [-126, 0]: bit patterns 0x80000000 .. 0xC2FC0000
-  const uint64_t first = 0x80000000ull, last = 0xC2FC0000ull;
+  // every fp32 x in [-126, 0] (bit patterns 0x80000000 .. 0xC2FC0000) and in
+  // [0, kExp2ArgMax] (0x00000000 .. the bits of kExp2ArgMax)
+  const uint64_t nneg = 0xC2FC0000ull - 0x80000000ull + 1;
+  const uint64_t total = nneg + __float_as_uint(kExp2ArgMax) + 1;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   double worst = 0.0;
-  for (uint64_t b = first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b <= last; b += stride) {
-    const float x = __uint_as_float((unsigned)b);
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const unsigned b = i < nneg ? (unsigned)(0x80000000ull + i) : (unsigned)(i - nneg);
+    const float x = __uint_as_float(b);
     const double ref = exp2((double)x);
     const double err = fabs((double)fast_exp2(x) - ref) / ref;
     worst = fmax(worst, err);

@@ -43,12 +43,18 @@ hipError_t launch_lm_head(const void* hidden, const int32_t* rows, int M, int R,
 hipError_t launch_rows_status(const int32_t* rows, int M, int R, int32_t* status, hipStream_t stream);
 
 // Error model of a fast confidence term t = exp2(fl32(fl32(x - m) * log2e))
-// against exp(x - m), for a = m - x >= 0:  |t / exp(x - m) - 1| <= kExpC1 * a +
-// kExpC2.  kExpC1 covers the two fp32 roundings of the argument, kExpC2 the
-// hardware exp2 (certified below 2^-22 by sfv_selfcheck_bounds; 2^-20 is used).
+// against exp(x - m), for a = m - x:  |t / exp(x - m) - 1| <= kExpC1 * |a| +
+// kExpC2.  kExpC1 covers the two fp32 roundings of the argument and log2e's
+// own, kExpC2 the hardware exp2 (certified below 2^-22 by sfv_selfcheck_bounds
+// for every argument in [-126, kExp2ArgMax]; 2^-20 is used).  The greedy terms
+// have a >= 0; the sampled sweep takes them against a reference at most
+// kLazyMargin below its running max, so a >= -kLazyMargin and the argument
+// stays below kLazyMargin * log2e < kExp2ArgMax.
 constexpr float kLog2eF = 1.44269504088896341f;
 constexpr float kExpC1 = 3.5f / 16777216.0f;
 constexpr float kExpC2 = 1.0f / 1048576.0f;
+constexpr float kLazyMargin = 4.0f;
+constexpr float kExp2ArgMax = 6.0f;
 
 // Greedy partial of one row over a range of vocabulary ids (a 128-id vocab
 // tile when written by the fused LM head): the max logit, the lowest id

@@ -408,7 +408,7 @@ int sfv_match_tree(const int32_t* state, const int32_t* next_state, const int32_
 
 /*
  * Device self-check of the fast-path bounds the commit relies on.  Sweeps
- * every 32-bit noise word and every fp32 argument in [-126, 0] of the fast
+ * every 32-bit noise word and every fp32 argument in [-126, 6] of the fast
  * exp2 and writes out[0] = max over all words of how far the exact Gumbel
  * value (fp64 logarithms, as the commit defines it) lies outside the bounds
  * of its bucket in the sweep's table (0: every word inside), and out[1] = max

@@ -230,7 +230,7 @@ def test_graph_replay_matches_eager(gpu_lib, idx, attn_with):
 
 def test_selfcheck_bounds(gpu_lib):
     out = torch.zeros(2, dtype=torch.float64, device="cuda")
-    say("self-check: all 2^32 noise words and all fp32 exp2 arguments in [-126, 0]")
+    say("self-check: all 2^32 noise words and all fp32 exp2 arguments in [-126, 6]")
     gpu_lib.sfv_selfcheck_bounds(out)
     torch.cuda.synchronize()
     g_err, e_rel = out.cpu().tolist()
