@@ -162,6 +162,8 @@ def test_greedy_partials_validation(lib):
     # from 33 rows on: one 16-byte partial per row and 256-id vocab tile
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 148, 151936, 4096)
     assert rc == sfv.SFV_OK and nb == (151936 + 255) // 256 * 148 * 16
+    rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 193, 151936, 4096)
+    assert rc == sfv.SFV_OK and nb == (151936 + 255) // 256 * 193 * 16
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 160, 1000, 128)
     assert rc == sfv.SFV_OK and nb == 4 * 160 * 16
     rc, nb = _ws(lib.sfv_lm_head_greedy_bytes, 161, 1000, 64)

@@ -147,6 +147,9 @@ def _compare(sweep, parts, state, N, k_max, parent=None, tau=0.0):
     (24, 32, 700, 128, 520, 3, 0.9),
     (12, 32, 384, 256, 33288, 1, 0.0),
     (20, 32, 600, 320, 40000, 2, 0.5),
+    # more than 256 vocab tiles for one row tile
+    (5, 32, 150, 128, 70000, 1, 0.0),
+    (9, 32, 148, 64, 151936, 2, 0.5),
 ])
 def test_partials_match_sweep(gpu_lib, B1, N, M, D, V, k_max, tau):
     rng = np.random.default_rng(M * 7 + V)

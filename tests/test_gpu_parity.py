@@ -557,7 +557,9 @@ def test_attention_ragged(gpu_lib, shape):
                                    (33, 128, 1000), (64, 4096, 4100), (100, 192, 777), (128, 64, 999),
                                    (180, 192, 1001), (192, 4096, 3000), (224, 256, 1001), (200, 320, 777),
                                    (300, 256, 33280), (512, 320, 33000), (520, 256, 40001),
-                                   (161, 256, 1001), (40, 64, 8), (33, 64, 255), (47, 192, 130)])
+                                   (161, 256, 1001), (40, 64, 8), (33, 64, 255), (47, 192, 130),
+                                   # more than 256 vocab tiles for one row tile (ragged vocab)
+                                   (100, 256, 70001), (192, 128, 65540), (33, 64, 151936)])
 def test_lm_head_ragged(gpu_lib, M, D, V):
     rng = np.random.default_rng(M)
     R = M + 3
