@@ -384,6 +384,40 @@ def test_tie_breaks(gpu_lib):
     assert res["commit_pos"][0, 0] == 0 and res["token"][0] == 5
 
 
+@pytest.mark.parametrize("T", [0.0, 1.0, 0.7])
+def test_commit_ramped_logits(gpu_lib, T):
+    """Logits that rise along the vocabulary by about 6 per 2048 ids (a lane's
+    step), so every lane's running max keeps moving and the sweep's confidence
+    sums are rescaled at every iteration; falling and sawtooth rows beside
+    them, and in branch 1 two masked positions with identical logits (equal
+    confidence: the lower position is committed).  A chain of 8 branches of
+    256 positions bounds the work items at 2048, so one workgroup sweeps each
+    item's whole vocabulary (10 iterations).  Tokens, positions and the walk
+    are the oracle's; conf within 1e-5."""
+    rng = np.random.default_rng(4321)
+    B1, N, V = 8, 256, 20480
+    st = rng.integers(0, V, (B1, N)).astype(np.int32)
+    for i in range(B1):
+        st[i, rng.choice(N, int(rng.integers(3, 8)), replace=False)] = O.MASK
+    st[1, 2] = st[1, 9] = O.MASK
+    parent = np.arange(-1, B1 - 1, dtype=np.int32)
+    rows = O.masked_rows(st)
+    ramp = np.linspace(0.0, 60.0, V, dtype=np.float32)
+    saw = (np.arange(V) % 4096).astype(np.float32) * np.float32(30.0 / 4096)
+    shapes = [ramp, ramp[::-1].copy(), saw]
+    lg = np.stack([rng.standard_normal(V).astype(np.float32) + shapes[k % 3]
+                   for k in range(rows.size)]).astype(np.float32)
+    ra, rb = int(np.flatnonzero(rows == 1 * N + 2)[0]), int(np.flatnonzero(rows == 1 * N + 9)[0])
+    lg[rb] = lg[ra]
+    lg[ra, 77] = lg[ra].max() + 8.0  # branch 1's most confident positions, tied
+    lg[rb, 77] = lg[ra, 77]
+    say(f"ramped logits T={T} B1={B1} N={N} M={rows.size} V={V}")
+    x = dict(state=st, parent=parent)
+    res = _run_commit_match(st, parent, V, T, 11, 500, 64, lg)
+    check_commit_match(x, res, T, 11, 500, 64, 1, logits_host=lg)
+    assert res["commit_pos"][1, 0] == 2
+
+
 @pytest.mark.parametrize("T", [1.0, 0.7])
 def test_gumbel_key_near_ties(gpu_lib, T):
     """Thousands of ids per row whose Gumbel keys fl32(fl32(l/T) + g) lie
