@@ -141,3 +141,12 @@ def test_lower_bound_from_upper_bound(gen, table):
     # without the rounding term the bound fails at large |x|
     slack = np.float32(np.float32(width) * np.float32(1.01))
     assert ((up - slack).astype(np.float32) > key).any()
+    # extreme magnitudes and subnormal logits
+    xe = np.array([3e38, -3e38, 1e30, -1e30, 1e-40, -1e-40, 0.0, 65504.0, -65504.0], np.float32)
+    we = rng.integers(0, 2 ** 32, (xe.size, 64), dtype=np.uint64).astype(np.uint32)
+    xe = np.repeat(xe[:, None], 64, axis=1)
+    with np.errstate(over="ignore"):
+        ke = (xe + O.gumbel_from_words(we)).astype(np.float32)
+        ue = (xe + hi[gen.bucket_of_word(we)]).astype(np.float32)
+        le = _lower_from_upper(ue, width)
+    assert np.isfinite(le).all() and (le <= ke).all() and (ke <= ue).all()
