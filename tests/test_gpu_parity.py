@@ -384,30 +384,27 @@ def test_tie_breaks(gpu_lib):
     assert res["commit_pos"][0, 0] == 0 and res["token"][0] == 5
 
 
-@pytest.mark.parametrize("T", [0.0, 1.0, 0.7])
+@pytest.mark.parametrize("T", [1.0, 0.7])
 def test_commit_ramped_logits(gpu_lib, T):
-    """Logits that rise along the vocabulary by about 6 per 2048 ids (a lane's
-    step), so every lane's running max keeps moving and the sweep's confidence
-    sums are rescaled at every iteration; falling and sawtooth rows beside
-    them, and in branch 1 two masked positions with identical logits (equal
-    confidence: the lower position is committed).  A chain of 8 branches of
-    256 positions bounds the work items at 2048, so one workgroup sweeps each
-    item's whole vocabulary (10 iterations).  Tokens, positions and the walk
-    are the oracle's; conf within 1e-5."""
+    """Logits that rise along the vocabulary by more than 4 per 2048 ids (a
+    lane's step), so every lane's running max keeps moving and the sampled
+    sweep's confidence sums are rescaled at every iteration; falling and
+    sawtooth rows beside them, and in branch 1 two masked positions with
+    identical logits (equal confidence: the lower position is committed).  A
+    chain of 8 branches of 64 positions, all masked (M = 512), over the full
+    vocabulary: the sweep takes 4 vocab ranges of 19 iterations.  Tokens,
+    positions and the walk are the oracle's; conf within 1e-5."""
     rng = np.random.default_rng(4321)
-    B1, N, V = 8, 256, 20480
-    st = rng.integers(0, V, (B1, N)).astype(np.int32)
-    for i in range(B1):
-        st[i, rng.choice(N, int(rng.integers(3, 8)), replace=False)] = O.MASK
-    st[1, 2] = st[1, 9] = O.MASK
+    B1, N, V = 8, 64, 151936
+    st = np.full((B1, N), O.MASK, np.int32)
     parent = np.arange(-1, B1 - 1, dtype=np.int32)
     rows = O.masked_rows(st)
-    ramp = np.linspace(0.0, 60.0, V, dtype=np.float32)
-    saw = (np.arange(V) % 4096).astype(np.float32) * np.float32(30.0 / 4096)
+    ramp = np.arange(V, dtype=np.float32) * np.float32(6.0 / 2048)
+    saw = (np.arange(V) % 8192).astype(np.float32) * np.float32(30.0 / 8192)
     shapes = [ramp, ramp[::-1].copy(), saw]
     lg = np.stack([rng.standard_normal(V).astype(np.float32) + shapes[k % 3]
                    for k in range(rows.size)]).astype(np.float32)
-    ra, rb = int(np.flatnonzero(rows == 1 * N + 2)[0]), int(np.flatnonzero(rows == 1 * N + 9)[0])
+    ra, rb = 1 * N + 2, 1 * N + 9  # rows are (i, n) in order: all positions are masked
     lg[rb] = lg[ra]
     lg[ra, 77] = lg[ra].max() + 8.0  # branch 1's most confident positions, tied
     lg[rb, 77] = lg[ra, 77]
