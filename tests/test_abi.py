@@ -72,7 +72,7 @@ def test_attend_split_plan(lib, B1, N, L, Hq, Hkv, d, splits):
     split needs no workspace unless the unsplit grid overshoots whole rounds
     of 512 workgroups by at most 128: then the last ceil(overshoot / Hkv) row
     tiles of every kv head are split over the context (at least two 64-key
-    tiles a split, at most 16 splits, about 512 workgroups) and only their
+    tiles a split, at most 8 splits, up to 512 workgroups) and only their
     states need room."""
     rc, nb = _ws(lib.sfv_attend_workspace_bytes, B1, N, L, Hq, Hkv, d)
     assert rc == sfv.SFV_OK
@@ -84,12 +84,12 @@ def test_attend_split_plan(lib, B1, N, L, Hq, Hkv, d, splits):
     over = wgs % 512
     if wgs > 512 and 0 < over <= 128 and L >= 128:
         tail = -(-over // Hkv)
-        ts = min(512 // (tail * Hkv), L // 128, 16)
+        ts = min(512 // (tail * Hkv), L // 128, 8)
         chunk = -(-(-(-L // ts)) // 64) * 64
         ts = -(-L // chunk)
         assert nb == ts * Hkv * tail * 128 * (d + 2) * 4, (nb, tail, ts)
         if (B1, N, L) == (33, 64, 4096):
-            assert (tail, ts) == (4, 16)
+            assert (tail, ts) == (4, 8)
     else:
         assert nb == 0
 
